@@ -1,0 +1,223 @@
+"""Benchmark of the grouped W4A8 MoE GEMM hot path on one MI355X.
+
+One step = routing prep (histogram, offsets, row map) + the grouped GEMM
+(whose kernels apply the per-expert tile plan in their prologue) over one
+batch of seeded synthetic inputs already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--layout 0|1]
+
+Prints one JSON line.  value = whole-step TFLOP/s (2*R*N*K per step);
+roofline = the grouped GEMM launch (both kernel classes, one call) against
+HBM (8 TB/s) or the FP8-rate MFMA peak (5.0 PFLOP/s); cpu_baseline = the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+MFMA_FP8_PEAK_TFS = 5000.0  # MI355X dense FP8 MFMA, published (FP8 x FP4 runs at this rate)
+INFINITY_CACHE_BYTES = 256 << 20
+
+DEFAULT_STEPS = {"prefill_gateup": 20}
+BOUND = {"prefill_gateup": "mfma", "prefill_down": "mfma"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(counts, E, N, K):
+    R = int(sum(counts))
+    hit = sum(1 for c in counts if c > 0)
+    return (hit * N * K * (0.5 + 1.0 / 32) + R * K + R * (K // 128) * 4 + R * N * 2 + 4 * (E + 1))
+
+
+def cpu_baseline(p, off, layout, budget_s=20.0):
+    """Time the oracle on a bounded sample of the workload: whole experts in
+    order until about budget_s seconds of CPU work, scaled to TFLOP/s."""
+    import numpy as np
+    from oracle import grouped_gemm_bf16
+
+    A = p.A.cpu().numpy()
+    SA = p.SA.cpu().numpy()
+    B = p.B.cpu().numpy()
+    SB = p.SB.cpu().numpy()
+    flops = 0.0
+    experts = 0
+    rows_done = 0
+    t0 = time.perf_counter()
+    G = p.K // 128
+    for e in range(p.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        hi = min(hi, lo + 2048)  # cap the rows of one expert in the sample
+        sa = SA[lo:hi]
+        if layout == 1:
+            sa_l = sa.T.copy().reshape(-1)
+        else:
+            sa_l = sa.reshape(-1)
+        grouped_gemm_bf16(A[lo:hi], sa_l, layout, B[e:e + 1], SB[e:e + 1],
+                          np.array([0, hi - lo], dtype=np.int32))
+        flops += 2.0 * (hi - lo) * p.N * p.K
+        experts += 1
+        rows_done += hi - lo
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{experts} experts, {rows_done} rows (<=2048 per expert) of the same "
+                      f"workload, numpy fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_gateup")
+    ap.add_argument("--layout", type=int, default=None, help="0 row-major, 1 M-major input scales")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    name = args.config
+    cfg = synth.CONFIGS[name]
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(name, 50)
+    layout = args.layout if args.layout is not None else (1 if name == "prefill_gateup" else 0)
+    w4a8.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"generating {name} on {'cuda' if name == 'prefill_gateup' else 'cpu'}")
+    gen_dev = "cuda" if name == "prefill_gateup" else "cpu"
+    p = synth.make_problem(name, device=gen_dev)
+    ids = p.topk_ids.to(dev)
+    A = p.A.to(dev)
+    SA = (p.SA if layout == 0 else synth.to_m_major(p.SA)).to(dev)
+    weight_bytes = p.B.numel() + p.SB.numel()
+    # rotate weight copies so that timed reads come from HBM, not the 256 MB Infinity Cache
+    nrot = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / weight_bytes) + 1)
+    Bs = [p.B.to(dev)] + [p.B.to(dev).clone() for _ in range(nrot - 1)]
+    SBs = [p.SB.to(dev)] + [p.SB.to(dev).clone() for _ in range(nrot - 1)]
+    counts_d = torch.empty(p.E, dtype=torch.int32, device=dev)
+    off_d = torch.empty(p.E + 1, dtype=torch.int32, device=dev)
+    rows_d = torch.empty(p.R, dtype=torch.int32, device=dev)
+    C = torch.empty((p.R, p.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident: R={p.R} N={p.N} K={p.K} E={p.E}, {nrot} weight copies")
+
+    def step(i):
+        w4a8.route_prep(ids, p.E, counts_d, off_d, rows_d)
+        w4a8.grouped_gemm(A, SA, layout, Bs[i % nrot], SBs[i % nrot], off_d, out=C)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # whole-step timing
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+
+    # per-launch timing of the grouped GEMM call, on the stream it is launched on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        w4a8.route_prep(ids, p.E, counts_d, off_d, rows_d)
+        ev[i][0].record()
+        w4a8.grouped_gemm(A, SA, layout, Bs[i % nrot], SBs[i % nrot], off_d, out=C)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    gemm_ms = [a.elapsed_time(b) for a, b in ev]
+    gemm_med = statistics.median(gemm_ms)
+    log(f"timed {steps} steps: {ms_per_step * 1e3:.1f} us/step, gemm median {gemm_med * 1e3:.1f} us")
+
+    counts = counts_d.cpu().numpy()
+    off = off_d.cpu().numpy()
+    flops = 2.0 * p.R * p.N * p.K
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    nbytes = algorithmic_bytes(counts, p.E, p.N, p.K)
+    bound = BOUND.get(name, "hbm")
+    if bound == "hbm":
+        achieved = nbytes / (gemm_med * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (gemm_med * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(p, off, layout, args.cpu_budget)
+
+    layout_name = "M-major" if layout == 1 else "row-major"
+    out = {
+        "metric": "grouped W4A8 GEMM TFLOP/s (routing prep + grouped GEMM per step)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{name}: E={p.E} top_k={p.top_k} tokens={p.T} routed_rows={p.R} "
+                        f"N={p.N} K={p.K} {cfg['routing']} routing, {layout_name} input scales",
+            "experts_with_rows": int((counts > 0).sum()),
+            "max_rows_per_expert": int(counts.max()) if len(counts) else 0,
+            "gemm_us_median": round(gemm_med * 1e3, 2),
+            "gemm_us_p10_p90": [round(float(np.percentile(gemm_ms, 10)) * 1e3, 2),
+                                round(float(np.percentile(gemm_ms, 90)) * 1e3, 2)],
+            "algorithmic_bytes": int(nbytes),
+            "flop": flops,
+            "weight_copies_rotated": nrot,
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

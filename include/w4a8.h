@@ -1,0 +1,166 @@
+/*
+ * w4a8.h -- C ABI of the grouped-contiguous W4A8 MoE expert GEMM for MI355X (gfx950).
+ *
+ * The operation (humming PR #129, title, intro and the "Results" benchmark
+ * command): a grouped GEMM over experts whose routed rows are stored
+ * contiguously by expert, with
+ *   A  FP8 E4M3 activations, one fp32 scale per (row, 128-K group), the scales
+ *      stored row-major or M-major ("--input_scale_group_size 128",
+ *      "--use_m_major_input_scale");
+ *   B  MXFP4 E2M1 expert weights, one E8M0 scale per 32 K
+ *      ("--b_dtype float4e2m1 --bs_dtype float8e8m0 --weight_scale_group_size 32");
+ *   C  bf16 output ("--c_dtype bfloat16");
+ * and the M tile of every expert chosen from that expert's own row count
+ * (same page, commit 1 "Row-major tile model" and commit 2 "Small-expert seed
+ * tile").  The routing prep that produces the contiguous grouping keeps a
+ * per-expert histogram and prefix arrays, as the MoE planning kernel of
+ * MoonEP PR #38 (background section) does.
+ *
+ *   C[r, n] = bf16_rne( sum_k e4m3(A[r,k]) * SA(r, k/128)
+ *                             * e2m1(B[e,n,k]) * 2^(SB[e,n,k/32] - 127) ),
+ *   e = the expert with offsets[e] <= r < offsets[e+1].
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *_dev are device pointers (hipMalloc / torch CUDA memory);
+ *     pointers named *_host are host pointers.  The caller owns every buffer;
+ *     the library keeps no pointer after the call's stream work completes and
+ *     never allocates or frees memory on the call path.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  All device work is enqueued on it asynchronously; no entry
+ *     point synchronises the host, so calls may be captured in a HIP graph.
+ *   - Return value: a w4a8_status.  Argument errors the host can see are
+ *     reported before anything is launched; a HIP launch failure returns
+ *     W4A8_ERR_HIP.  w4a8_last_error() gives a per-thread text for the last
+ *     non-OK return.
+ *   - Conditions only the device can see (offsets not starting at 0 or
+ *     decreasing) make the kernels write nothing; w4a8_plan reports them in
+ *     its header's status word.
+ *   - Only gfx950 devices are supported (W4A8_ERR_DEVICE otherwise).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A8_OK = 0,
+  W4A8_ERR_NULL = 1,      /* a required pointer is NULL */
+  W4A8_ERR_SHAPE = 2,     /* E, N, K, T or top_k outside the supported range */
+  W4A8_ERR_LAYOUT = 3,    /* unknown a_scale_layout */
+  W4A8_ERR_ALIGN = 4,     /* a pointer is not aligned as documented */
+  W4A8_ERR_CAPACITY = 5,  /* a caller buffer is too small */
+  W4A8_ERR_DEVICE = 6,    /* current device is not gfx950 or cannot be queried */
+  W4A8_ERR_HIP = 7        /* a HIP runtime call failed */
+} w4a8_status;
+
+/* Input-scale layouts (humming PR #129: row-major and M-major input scales). */
+enum {
+  W4A8_SCALE_ROW_MAJOR = 0, /* a_scales fp32 [R][K/128]: SA(r,g) at r*(K/128)+g */
+  W4A8_SCALE_M_MAJOR = 1    /* a_scales fp32 [K/128][R]: SA(r,g) at g*R+r, R = offsets[E] */
+};
+
+/* Limits of this version. */
+#define W4A8_MAX_EXPERTS 1024
+
+/*
+ * w4a8_route_prep -- routing histogram, exclusive-scan offsets and row map.
+ *
+ * topk_ids_dev       int32 [T*top_k], row-major [T][top_k]: expert of each
+ *                    (token, slot).  Ids outside [0, E) are ignored.
+ * counts_dev         out int32 [E]: slots routed to each expert.
+ * expert_offsets_dev out int32 [E+1]: offsets[0] = 0, offsets[e+1] =
+ *                    offsets[e] + counts[e]; offsets[E] = R, the routed rows.
+ * row_of_slot_dev    out int32 [T*top_k]: the grouped row of each slot; rows
+ *                    of one expert keep the flat (token, slot) order (a stable
+ *                    counting sort), so the result is unique.  -1 for an
+ *                    ignored id.
+ * Limits: 1 <= E <= W4A8_MAX_EXPERTS, 0 <= T, 1 <= top_k, T*top_k < 2^31.
+ * Alignment: 4 bytes for every pointer.
+ */
+int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E,
+                    int32_t* counts_dev, int32_t* expert_offsets_dev,
+                    int32_t* row_of_slot_dev, void* stream);
+
+/*
+ * w4a8_plan_bytes -- bytes a plan buffer needs for E experts and at most
+ * max_total_rows routed rows (host only; no device work).  Returns 0 for
+ * E outside [1, W4A8_MAX_EXPERTS] or a negative row count.
+ */
+size_t w4a8_plan_bytes(int E, int64_t max_total_rows);
+
+/*
+ * w4a8_plan -- per-expert tile list built on the device from expert offsets
+ * (the tile rule that the GEMM kernels apply in their own prologue, exposed
+ * for inspection and for callers that want the list).
+ *
+ * expert_offsets_dev int32 [E+1] (as produced by w4a8_route_prep).
+ * plan_dev           out int32 buffer of plan_bytes bytes:
+ *   header [8]: status (0 ok, 1 offsets invalid, 2 buffer too small),
+ *               m-tiles, streaming-class m-tiles, MFMA-class m-tiles,
+ *               streaming work items, MFMA work items, padded rows, rows R
+ *   then 4 int32 per m-tile: expert, first row, rows, tile_m | class << 16
+ *   (class 1 = weight-streaming small-M kernel, 2 = MFMA kernel); streaming
+ *   tiles first, then MFMA tiles, each in (expert, row) order.
+ * Rule for an expert with rows r (integer only; constants by w4a8_plan_params):
+ *   r == 0 -> no tile; r <= S_MAX -> one streaming tile, tile_m = ceil16(r);
+ *   r > S_MAX -> n = ceil(r / T_MAX) MFMA tiles, tile_m = ceil16(ceil(r / n)).
+ * Limits: as w4a8_grouped_gemm.  plan_bytes must hold at least the header
+ * (W4A8_ERR_CAPACITY otherwise); a plan with more tiles than fit sets status 2
+ * and writes the tiles that fit.  Alignment: 4 bytes.
+ */
+int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K,
+              void* plan_dev, size_t plan_bytes, void* stream);
+
+/*
+ * w4a8_grouped_gemm -- the grouped W4A8 GEMM.
+ *
+ * A_fp8_dev          uint8 [R][K] E4M3 codes; rows offsets[e]..offsets[e+1]-1
+ *                    belong to expert e.  16-byte aligned.
+ * a_scales_dev       fp32 per (row, 128-K group) in the given layout
+ *                    (W4A8_SCALE_ROW_MAJOR or W4A8_SCALE_M_MAJOR; for M-major
+ *                    the leading dimension is R = offsets[E], read on the
+ *                    device).  4-byte aligned.
+ * B_fp4_dev          uint8 [E][N][K/2] E2M1 codes, K-contiguous per output
+ *                    column; element 2j in bits 3:0, element 2j+1 in bits 7:4.
+ *                    16-byte aligned.
+ * b_scales_e8m0_dev  uint8 [E][N][K/32] E8M0 codes.  4-byte aligned.
+ * expert_offsets_dev int32 [E+1], offsets[0] = 0, nondecreasing.
+ * C_bf16_dev         out uint16 (bf16 bits) [R][N]; only rows < R are written.
+ *                    16-byte aligned.
+ * Limits: 1 <= E <= W4A8_MAX_EXPERTS; K % 128 == 0, K >= 128; N % 32 == 0,
+ * N >= 32; R*K and R*N below 2^62.  A, a_scales and C must hold R rows.
+ * Numerics: each 128-K group is reduced by a scaled MFMA in fp32 (E8M0 weight
+ * scales applied inside it), multiplied by its fp32 activation scale and
+ * accumulated in fp32; one RNE rounding to bf16 at the end.  NaN codes
+ * (E4M3 S.1111.111, E8M0 0xFF) propagate to the rows/columns they touch.
+ */
+int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                      const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                      const int32_t* expert_offsets_dev, int E, int N, int K,
+                      uint16_t* C_bf16_dev, void* stream);
+
+/*
+ * w4a8_plan_params -- the plan rule's constants, written to out_host[0..n-1]
+ * in this order: GRAN (m granularity), S_MAX, T_MAX, TN_STREAM (n width of a
+ * streaming work item), TN_MFMA (n width of an MFMA work item), plan header
+ * words, words per tile.  Returns the number of constants available (7) or
+ * -W4A8_ERR_NULL if out_host is NULL.
+ */
+int w4a8_plan_params(int32_t* out_host, int n);
+
+/* Human-readable name of a status code (static string). */
+const char* w4a8_status_string(int status);
+
+/* Per-thread detail of the last non-OK return of this thread ("" if none). */
+const char* w4a8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

@@ -1,0 +1,25 @@
+"""Grouped-contiguous W4A8 MoE expert GEMM for MI355X (gfx950).
+
+Thin ctypes binding over libw4a8.so (declared in include/w4a8.h).  Functions
+take torch CUDA tensors, check dtype/shape/device, and pass raw device
+pointers and the current HIP stream to the C ABI; every step of the
+computation runs in the library's HIP kernels.  Outputs are allocated with
+torch when the caller does not pass them.
+
+    route_prep(topk_ids, E)          -> counts, expert_offsets, row_of_slot
+    plan(expert_offsets, E, N, K)    -> int32 plan (header + tiles)
+    grouped_gemm(A, SA, layout, B, SB, expert_offsets, out=None) -> C (bf16)
+"""
+
+from ._lib import (  # noqa: F401
+    SCALE_M_MAJOR,
+    SCALE_ROW_MAJOR,
+    W4A8Error,
+    grouped_gemm,
+    lib_path,
+    load,
+    plan,
+    plan_bytes,
+    plan_params,
+    route_prep,
+)

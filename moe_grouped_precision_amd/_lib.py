@@ -1,0 +1,179 @@
+"""ctypes binding of libw4a8.so (argument marshalling only)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libw4a8.so")
+
+SCALE_ROW_MAJOR = 0
+SCALE_M_MAJOR = 1
+
+_STATUS = {0: "W4A8_OK", 1: "W4A8_ERR_NULL", 2: "W4A8_ERR_SHAPE", 3: "W4A8_ERR_LAYOUT",
+           4: "W4A8_ERR_ALIGN", 5: "W4A8_ERR_CAPACITY", 6: "W4A8_ERR_DEVICE", 7: "W4A8_ERR_HIP"}
+
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _declare(lib):
+    i32, i64, sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.w4a8_route_prep.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.w4a8_route_prep.restype = i32
+    lib.w4a8_plan_bytes.argtypes = [i32, i64]
+    lib.w4a8_plan_bytes.restype = sz
+    lib.w4a8_plan.argtypes = [vp, i32, i32, i32, vp, sz, vp]
+    lib.w4a8_plan.restype = i32
+    lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_plan_params.argtypes = [ctypes.POINTER(ctypes.c_int32), i32]
+    lib.w4a8_plan_params.restype = i32
+    lib.w4a8_status_string.argtypes = [i32]
+    lib.w4a8_status_string.restype = ctypes.c_char_p
+    lib.w4a8_last_error.argtypes = []
+    lib.w4a8_last_error.restype = ctypes.c_char_p
+
+
+def load(require_device: bool = True):
+    """Load libw4a8.so (once).  Raises if it is missing, or -- when
+    ``require_device`` -- if the current CUDA device is not gfx950."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m moe_grouped_precision_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        _declare(lib)
+        _lib = lib
+    if require_device:
+        if not torch.cuda.is_available():
+            raise RuntimeError("libw4a8 needs a visible MI355X (gfx950) GPU")
+        arch = torch.cuda.get_device_properties(torch.cuda.current_device()).gcnArchName
+        if not arch.startswith("gfx950"):
+            raise RuntimeError(f"libw4a8 supports gfx950 only, current device is {arch}")
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise W4A8Error(fn, status, _lib.w4a8_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def plan_params():
+    """(GRAN, S_MAX, T_MAX, TN_STREAM, TN_MFMA, header words, tile words)."""
+    lib = load(require_device=False)
+    out = (ctypes.c_int32 * 7)()
+    n = lib.w4a8_plan_params(out, 7)
+    return tuple(out[i] for i in range(n))
+
+
+def plan_bytes(E: int, max_total_rows: int) -> int:
+    return int(load(require_device=False).w4a8_plan_bytes(E, max_total_rows))
+
+
+def route_prep(topk_ids: torch.Tensor, E: int, counts=None, offsets=None, row_of_slot=None):
+    """topk_ids int32 [T, top_k] -> (counts [E], expert_offsets [E+1], row_of_slot [T*top_k])."""
+    lib = load()
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, top_k]")
+    T, k = topk_ids.shape
+    _need(topk_ids, "topk_ids", torch.int32)
+    dev = topk_ids.device
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if row_of_slot is None:
+        row_of_slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _need(counts, "counts", torch.int32, E)
+    _need(offsets, "expert_offsets", torch.int32, E + 1)
+    _need(row_of_slot, "row_of_slot", torch.int32, T * k)
+    _check("w4a8_route_prep", lib.w4a8_route_prep(_ptr(topk_ids), T, k, E, _ptr(counts),
+                                                 _ptr(offsets), _ptr(row_of_slot), _stream()))
+    return counts, offsets, row_of_slot
+
+
+def plan(expert_offsets: torch.Tensor, E: int, N: int, K: int, max_total_rows: Optional[int] = None,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device tile plan as an int32 tensor (8-word header + 4 words per m-tile)."""
+    lib = load()
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    if out is None:
+        if max_total_rows is None:
+            raise ValueError("give max_total_rows (an upper bound on offsets[E]) or out")
+        nbytes = lib.w4a8_plan_bytes(E, max_total_rows)
+        if nbytes == 0:
+            raise ValueError("invalid E or max_total_rows")
+        out = torch.zeros(nbytes // 4, dtype=torch.int32, device=expert_offsets.device)
+    _need(out, "plan", torch.int32)
+    _check("w4a8_plan", lib.w4a8_plan(_ptr(expert_offsets), E, N, K, _ptr(out), out.numel() * 4,
+                                      _stream()))
+    return out
+
+
+def grouped_gemm(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor, SB: torch.Tensor,
+                 expert_offsets: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[R, N] (torch.bfloat16) of the grouped W4A8 GEMM.
+
+    A uint8 [R, K] E4M3 codes; SA fp32 [R, K/128] (layout 0) or [K/128, R]
+    (layout 1); B uint8 [E, N, K/2] packed E2M1; SB uint8 [E, N, K/32] E8M0;
+    expert_offsets int32 [E+1] with offsets[E] == R.
+    """
+    lib = load()
+    if A.dim() != 2 or B.dim() != 3 or SB.dim() != 3:
+        raise ValueError("A must be [R, K], B [E, N, K/2], SB [E, N, K/32]")
+    R, K = A.shape
+    E, N, Kh = B.shape
+    if Kh * 2 != K or SB.shape != (E, N, K // 32):
+        raise ValueError("inconsistent K between A, B and SB")
+    _need(A, "A", torch.uint8)
+    _need(SA, "a_scales", torch.float32, R * (K // 128))
+    _need(B, "B", torch.uint8)
+    _need(SB, "b_scales", torch.uint8)
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=A.device)
+    if out.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("out must be bfloat16 (or 16-bit integer bits)")
+    _need(out, "out", out.dtype, R * N)
+    if R == 0:
+        return out  # no rows: nothing to compute
+    _check("w4a8_grouped_gemm", lib.w4a8_grouped_gemm(
+        _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
+        _ptr(out), _stream()))
+    return out

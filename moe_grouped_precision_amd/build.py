@@ -1,0 +1,84 @@
+"""Build libw4a8.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m moe_grouped_precision_amd.build          # build
+    python -m moe_grouped_precision_amd.build --check  # build, then list exported symbols
+
+The library is placed next to this file so that it travels with the source
+tree.  Every HIP source is compiled with packed-fp32 instructions disabled.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libw4a8.so")
+SOURCES = ["api.cpp", "prep.hip", "gemm.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libw4a8)")
+
+
+def compile_flags(debug: bool = False):
+    flags = [
+        f"--offload-arch={ARCH}",
+        "-std=c++17",
+        "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        "-I", CSRC,
+        "-Wall",
+    ]
+    flags += ["-O0", "-g"] if debug else ["-O3"]
+    return flags
+
+
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link libw4a8.so; returns the library path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="w4a8_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            obj = os.path.join(tmp, src.replace(".", "_") + ".o")
+            cmd = [cc, "-x", "hip", *compile_flags(debug), "-c", path, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libw4a8.so")
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stderr}")
+        shutil.copyfile(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    path = build(verbose="-v" in argv, debug="--debug" in argv)
+    print(path)
+    if "--check" in argv:
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+        print("\n".join(l for l in out.splitlines() if " w4a8_" in l))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+// C ABI of libw4a8: argument validation, per-device set-up, kernel dispatch.
+// Declarations and contracts: include/w4a8.h.
+#include "../../include/w4a8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "w4a8_device.h"
+#include "w4a8_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return W4A8_OK;
+}
+
+struct DeviceInfo {
+  bool ready = false;
+  bool supported = false;
+  int cus = 0;
+  int grid_stream = 0;
+  int grid_mfma = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Per-device set-up on first use: architecture check, CU count, occupancy.
+int device_info(const DeviceInfo** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4A8_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4A8_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(W4A8_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    if (d.supported) {
+      int bs = 0, bm = 0;
+      e = w4a8::occupancy_blocks_per_cu(&bs, &bm);
+      if (e != hipSuccess) return fail(W4A8_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+      d.grid_stream = d.cus * (bs > 0 ? bs : 1);
+      d.grid_mfma = d.cus * (bm > 0 ? bm : 1);
+    }
+    d.ready = true;
+  }
+  if (!d.supported) return fail(W4A8_ERR_DEVICE, "device %d is not gfx950", dev);
+  *out = &d;
+  return W4A8_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_gemm_shape(int E, int N, int K) {
+  if (E < 1 || E > W4A8_MAX_EXPERTS) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_EXPERTS);
+  if (K < 128 || K % 128) return fail(W4A8_ERR_SHAPE, "K=%d must be a positive multiple of 128", K);
+  if (N < 32 || N % 32) return fail(W4A8_ERR_SHAPE, "N=%d must be a positive multiple of 32", N);
+  return W4A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a8_status_string(int status) {
+  switch (status) {
+    case W4A8_OK: return "W4A8_OK";
+    case W4A8_ERR_NULL: return "W4A8_ERR_NULL";
+    case W4A8_ERR_SHAPE: return "W4A8_ERR_SHAPE";
+    case W4A8_ERR_LAYOUT: return "W4A8_ERR_LAYOUT";
+    case W4A8_ERR_ALIGN: return "W4A8_ERR_ALIGN";
+    case W4A8_ERR_CAPACITY: return "W4A8_ERR_CAPACITY";
+    case W4A8_ERR_DEVICE: return "W4A8_ERR_DEVICE";
+    case W4A8_ERR_HIP: return "W4A8_ERR_HIP";
+    default: return "W4A8_UNKNOWN_STATUS";
+  }
+}
+
+const char* w4a8_last_error(void) { return g_last_error; }
+
+int w4a8_plan_params(int32_t* out_host, int n) {
+  if (!out_host) return -W4A8_ERR_NULL;
+  const int32_t v[7] = {w4a8::GRAN, w4a8::S_MAX, w4a8::T_MAX, w4a8::TN_STREAM, w4a8::TN_MFMA,
+                        w4a8::PLAN_HEADER_WORDS, w4a8::PLAN_TILE_WORDS};
+  for (int i = 0; i < n && i < 7; ++i) out_host[i] = v[i];
+  return 7;
+}
+
+size_t w4a8_plan_bytes(int E, int64_t max_total_rows) {
+  if (E < 1 || E > W4A8_MAX_EXPERTS || max_total_rows < 0) return 0;
+  // every expert contributes at most floor(rows/T_MAX) + 1 tiles, and only
+  // experts with rows contribute
+  int64_t tiles = max_total_rows / w4a8::T_MAX + (max_total_rows < E ? max_total_rows : E);
+  return (size_t)(w4a8::PLAN_HEADER_WORDS + w4a8::PLAN_TILE_WORDS * tiles) * sizeof(int32_t);
+}
+
+int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E, int32_t* counts_dev,
+                    int32_t* expert_offsets_dev, int32_t* row_of_slot_dev, void* stream) {
+  if (E < 1 || E > W4A8_MAX_EXPERTS) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_EXPERTS);
+  if (T < 0 || top_k < 1) return fail(W4A8_ERR_SHAPE, "T=%d top_k=%d", T, top_k);
+  if ((int64_t)T * top_k >= (int64_t)1 << 31) return fail(W4A8_ERR_SHAPE, "T*top_k too large");
+  const int n = T * top_k;
+  if (!counts_dev || !expert_offsets_dev || (n > 0 && (!topk_ids_dev || !row_of_slot_dev)))
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(topk_ids_dev, 4) || !aligned(counts_dev, 4) || !aligned(expert_offsets_dev, 4) ||
+      !aligned(row_of_slot_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "pointers must be 4-byte aligned");
+  const DeviceInfo* d = nullptr;
+  int st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  hipError_t e = w4a8::launch_route_prep(topk_ids_dev, n, E, counts_dev, expert_offsets_dev,
+                                          row_of_slot_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "route_prep launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K, void* plan_dev,
+              size_t plan_bytes, void* stream) {
+  int st = check_gemm_shape(E, N, K);
+  if (st != W4A8_OK) return st;
+  if (!expert_offsets_dev || !plan_dev) return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(expert_offsets_dev, 4) || !aligned(plan_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "pointers must be 4-byte aligned");
+  const size_t words = plan_bytes / sizeof(int32_t);
+  if (words < (size_t)w4a8::PLAN_HEADER_WORDS)
+    return fail(W4A8_ERR_CAPACITY, "plan buffer of %zu bytes cannot hold the header", plan_bytes);
+  size_t max_tiles = (words - w4a8::PLAN_HEADER_WORDS) / w4a8::PLAN_TILE_WORDS;
+  if (max_tiles > (size_t)0x7fffffff) max_tiles = 0x7fffffff;
+  const DeviceInfo* d = nullptr;
+  st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  hipError_t e = w4a8::launch_plan(expert_offsets_dev, E, N, (int32_t*)plan_dev, (int)max_tiles,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                      const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                      const int32_t* expert_offsets_dev, int E, int N, int K, uint16_t* C_bf16_dev,
+                      void* stream) {
+  int st = check_gemm_shape(E, N, K);
+  if (st != W4A8_OK) return st;
+  if (a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR)
+    return fail(W4A8_ERR_LAYOUT, "a_scale_layout=%d is neither row-major (0) nor M-major (1)", a_scale_layout);
+  if (!A_fp8_dev || !a_scales_dev || !B_fp4_dev || !b_scales_e8m0_dev || !expert_offsets_dev || !C_bf16_dev)
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(A_fp8_dev, 16) || !aligned(B_fp4_dev, 16) || !aligned(C_bf16_dev, 16) ||
+      !aligned(a_scales_dev, 4) || !aligned(b_scales_e8m0_dev, 4) || !aligned(expert_offsets_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "A, B, C need 16-byte and scales/offsets 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev,
+                      C_bf16_dev, E, N, K, a_scale_layout};
+  hipError_t e = w4a8::launch_grouped_gemm(args, d->grid_stream, d->grid_mfma, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

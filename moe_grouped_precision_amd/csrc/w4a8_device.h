@@ -1,0 +1,158 @@
+// Device-side pieces shared by the prep, plan and GEMM kernels of libw4a8:
+// the per-expert tile rule, block-wide scans, bf16 rounding and the plan
+// prologue that every GEMM workgroup runs.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------------------
+// Tile rule.  The pages ask that each expert's M tile come from that expert's
+// own row count (humming PR #129, commit 1 "Row-major tile model"): a fixed
+// M128 tile gives experts routed slightly past a multiple of 128 an extra,
+// mostly empty tile, while rows that fill tiles exactly must get full tiles
+// (last note under that page's tables).  Small experts go to a separate
+// small-M schedule below a cutoff (commit 2 "Small-expert seed tile").
+// Constants are this library's own: GRAN is one MFMA block of rows, S_MAX the
+// largest expert the weight-streaming kernel serves (four MFMA blocks), T_MAX
+// the MFMA kernel's largest m-tile.
+// ---------------------------------------------------------------------------
+constexpr int GRAN = 16;
+constexpr int S_MAX = 64;
+constexpr int T_MAX = 128;
+constexpr int TN_STREAM = 32;
+constexpr int TN_MFMA = 256;
+constexpr int PLAN_HEADER_WORDS = 8;
+constexpr int PLAN_TILE_WORDS = 4;
+
+constexpr int CLASS_NONE = 0;
+constexpr int CLASS_STREAM = 1;
+constexpr int CLASS_MFMA = 2;
+
+constexpr int PLAN_OK = 0;
+constexpr int PLAN_BAD_OFFSETS = 1;
+constexpr int PLAN_CAPACITY = 2;
+
+constexpr int MAX_EXPERTS = 1024;
+
+struct TileChoice {
+  int cls;
+  int tile_m;
+  int n_m;
+};
+
+__host__ __device__ inline TileChoice tile_rule(int rows) {
+  TileChoice t;
+  if (rows <= 0) {
+    t.cls = CLASS_NONE; t.tile_m = 0; t.n_m = 0;
+  } else if (rows <= S_MAX) {
+    t.cls = CLASS_STREAM; t.tile_m = (rows + GRAN - 1) / GRAN * GRAN; t.n_m = 1;
+  } else {
+    t.cls = CLASS_MFMA;
+    t.n_m = (rows + T_MAX - 1) / T_MAX;
+    int per = (rows + t.n_m - 1) / t.n_m;
+    t.tile_m = (per + GRAN - 1) / GRAN * GRAN;
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one int per thread (wave64 shuffles + LDS).
+// `wave_tot` must hold blockDim.x/64 ints.  Returns the exclusive prefix and
+// writes the block total to *total.  All threads of the block must call it.
+// ---------------------------------------------------------------------------
+__device__ inline int block_exclusive_scan(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < nwaves ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(t, d, 64);
+      if (lane >= d) t += y;
+    }
+    if (lane < nwaves) wave_tot[lane] = t;  // inclusive wave totals
+  }
+  __syncthreads();
+  int base = wave > 0 ? wave_tot[wave - 1] : 0;
+  int tot = wave_tot[nwaves - 1];
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Plan prologue run by every GEMM workgroup: offsets into LDS, validity check,
+// and the exclusive scan of the m-tile counts of one class.
+//   s_off[0..E]   expert offsets
+//   s_base[0..E]  first m-tile of each expert within the class; s_base[E] = total
+// Returns false (uniformly across the block) if the offsets are invalid.
+// ---------------------------------------------------------------------------
+__device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int cls,
+                                     int* s_off, int* s_base, int* s_wave) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += blockDim.x) s_off[i] = offsets[i];
+  __syncthreads();
+  int bad = 0;
+  for (int i = tid; i < E; i += blockDim.x) bad |= (s_off[i + 1] < s_off[i]);
+  if (tid == 0) bad |= (s_off[0] != 0);
+  bad = __syncthreads_or(bad);
+  if (bad) return false;
+  // each thread owns a contiguous run of experts
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    int e = e0 + i;
+    if (e < E) {
+      TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
+      local += (t.cls == cls) ? t.n_m : 0;
+    }
+  }
+  int total;
+  int run = block_exclusive_scan(local, s_wave, &total);
+  for (int i = 0; i < per; ++i) {
+    int e = e0 + i;
+    if (e < E) {
+      s_base[e] = run;
+      TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
+      run += (t.cls == cls) ? t.n_m : 0;
+    }
+  }
+  if (tid == 0) s_base[E] = total;
+  __syncthreads();
+  return true;
+}
+
+// Expert owning class-local m-tile `mt`: the e with s_base[e] <= mt < s_base[e+1].
+__device__ inline int expert_of_tile(const int* s_base, int E, int mt) {
+  int lo = 0, hi = E;  // invariant: s_base[lo] <= mt < s_base[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (s_base[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace w4a8

@@ -1,0 +1,28 @@
+// Host-side launch interface between the C ABI layer (api.cpp) and the kernel
+// translation units (prep.hip, gemm.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+struct GemmArgs {
+  const uint8_t* A;        // [R][K] E4M3 codes
+  const float* SA;         // per (row, 128-K group), layout below
+  const uint8_t* B;        // [E][N][K/2] packed E2M1
+  const uint8_t* SB;       // [E][N][K/32] E8M0
+  const int32_t* offsets;  // [E+1]
+  uint16_t* C;             // [R][N] bf16 bits
+  int E, N, K, layout;     // layout 0 row-major, 1 M-major
+};
+
+hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* row_of_slot, hipStream_t stream);
+hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int max_tiles,
+                       hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmArgs& args, int grid_stream, int grid_mfma,
+                               hipStream_t stream);
+hipError_t occupancy_blocks_per_cu(int* stream_blocks, int* mfma_blocks);
+
+}  // namespace w4a8

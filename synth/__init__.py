@@ -15,5 +15,6 @@ from .generate import (  # noqa: F401
     make_routing,
     quantize_fp8_rows,
     quantize_mxfp4,
+    random_codes_problem,
     to_m_major,
 )

@@ -181,3 +181,25 @@ def make_problem(name: str, device: str = "cpu", *, T: Optional[int] = None,
         w = 0.02 * torch.randn((N_, K_), generator=gb, dtype=torch.float32, device=device)
         B[e], SB[e] = quantize_mxfp4(w)
     return Problem(name, E_, T_, k_, N_, K_, ids, A, SA, B, SB)
+
+
+def random_codes_problem(counts, N: int, K: int, seed: int, sb_lo: int = 112, sb_hi: int = 132,
+                         device: str = "cpu"):
+    """Raw random codes for edge-case tests (not a quantised workload).
+
+    ``counts`` rows per expert (rows are laid out contiguously in expert
+    order); A codes avoid the two E4M3 NaN codes, SA is U(0.01, 4) fp32,
+    B is any byte, SB is uniform in [sb_lo, sb_hi).  Returns
+    (A, SA_row_major, B, SB, offsets) as CPU tensors (offsets int32 [E+1]).
+    """
+    E = len(counts)
+    g = torch.Generator().manual_seed(seed)
+    R = int(sum(counts))
+    A = torch.randint(0, 256, (R, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x38
+    SA = torch.rand((R, K // 128), generator=g, dtype=torch.float32) * 4 + 0.01
+    B = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    SB = torch.randint(sb_lo, sb_hi, (E, N, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+    offsets = torch.zeros(E + 1, dtype=torch.int32)
+    offsets[1:] = torch.cumsum(torch.tensor(list(counts), dtype=torch.int64), 0).to(torch.int32)
+    return A, SA, B, SB, offsets

@@ -1,0 +1,105 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+reports its plan constants, and rejects bad arguments before any device work
+(every call here returns from host-side validation; no kernel is launched)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import moe_grouped_precision_amd as w4a8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a8_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4a8.lib_path()):
+        pytest.fail("libw4a8.so is not built (python -m moe_grouped_precision_amd.build)")
+    return w4a8.load(require_device=False)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "w4a8_grouped_gemm" in names and "w4a8_plan" in names and "w4a8_route_prep" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", w4a8.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (w4a8_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_plan_params_match_oracle(lib):
+    assert w4a8.plan_params() == oracle.PLAN_PARAMS
+
+
+def test_plan_bytes_bound(lib):
+    from oracle import plan as P
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        E = int(rng.integers(1, 64))
+        counts = rng.integers(0, 600, size=E) * (rng.random(E) < 0.7)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        need = len(oracle.plan_ref(off, E, 256)) * 4
+        assert w4a8.plan_bytes(E, int(off[-1])) >= need
+    assert w4a8.plan_bytes(0, 10) == 0 and w4a8.plan_bytes(1025, 10) == 0
+    assert w4a8.plan_bytes(4, -1) == 0
+    assert w4a8.plan_bytes(8, 0) == P.HEADER_WORDS * 4
+
+
+def test_status_strings(lib):
+    assert lib.w4a8_status_string(0) == b"W4A8_OK"
+    assert lib.w4a8_status_string(4) == b"W4A8_ERR_ALIGN"
+    assert lib.w4a8_status_string(99) == b"W4A8_UNKNOWN_STATUS"
+    assert lib.w4a8_plan_params(None, 7) == -1
+
+
+P16 = ctypes.c_void_p(1 << 20)   # a 16-byte aligned, never dereferenced address
+P4 = ctypes.c_void_p((1 << 20) + 4)
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P16, P16, 0, P16, P16, P16, 0, 256, 512, P16, NUL), 2),      # E = 0
+    ((P16, P16, 0, P16, P16, P16, 1025, 256, 512, P16, NUL), 2),   # E too large
+    ((P16, P16, 0, P16, P16, P16, 8, 256, 500, P16, NUL), 2),      # K % 128
+    ((P16, P16, 0, P16, P16, P16, 8, 48, 512, P16, NUL), 2),       # N % 32
+    ((P16, P16, 2, P16, P16, P16, 8, 256, 512, P16, NUL), 3),      # bad layout
+    ((NUL, P16, 0, P16, P16, P16, 8, 256, 512, P16, NUL), 1),      # null A
+    ((P16, P16, 0, P16, P16, P16, 8, 256, 512, NUL, NUL), 1),      # null C
+    ((P4, P16, 0, P16, P16, P16, 8, 256, 512, P16, NUL), 4),       # misaligned A
+    ((P16, P16, 0, P16, P16, P16, 8, 256, 512, P4, NUL), 4),       # misaligned C
+])
+def test_gemm_host_validation(lib, args, status):
+    assert lib.w4a8_grouped_gemm(*args) == status
+    assert lib.w4a8_last_error() != b""
+
+
+def test_plan_and_route_host_validation(lib):
+    assert lib.w4a8_plan(P16, 8, 256, 512, P16, 16, NUL) == 5        # buffer < header
+    assert lib.w4a8_plan(NUL, 8, 256, 512, P16, 1024, NUL) == 1
+    assert lib.w4a8_plan(P16, 8, 250, 512, P16, 1024, NUL) == 2
+    assert lib.w4a8_route_prep(P16, 4, 2, 0, P16, P16, P16, NUL) == 2
+    assert lib.w4a8_route_prep(P16, -1, 2, 8, P16, P16, P16, NUL) == 2
+    assert lib.w4a8_route_prep(P16, 4, 2, 8, NUL, P16, P16, NUL) == 1
+    assert lib.w4a8_route_prep(ctypes.c_void_p((1 << 20) + 2), 4, 2, 8, P16, P16, P16, NUL) == 4
+
+
+def test_binding_fails_loudly_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(RuntimeError):
+        w4a8.load(require_device=True)

@@ -1,0 +1,174 @@
+"""GPU grouped GEMM against the CPU oracle.
+
+Bar (elementwise): |gpu - ref| / max(rms(ref), |ref|) <= 8e-3 on seeded
+workloads; exact bits on inputs whose result is exactly representable
+(all-ones and one-hot rows with power-of-two activation scales); row-major
+and M-major scales bit-identical; repeated calls bit-identical.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import TOL, bits_of, parity_error, sample_rows, to_device
+from oracle import bf16_rne_bits, grouped_gemm_bf16, plan as oplan, route_ref
+from oracle.gemm import rows_gemm_f64, sa_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(lib, A, SA, layout, B, SB, off_dev):
+    C = lib.grouped_gemm(A, SA, layout, B, SB, off_dev)
+    torch.cuda.synchronize()
+    return C
+
+
+def _full_config(lib, name, layout):
+    p = synth.make_problem(name)
+    d = to_device(p)
+    _, off_dev, _ = lib.route_prep(d["ids"], p.E)
+    _, off, _ = route_ref(p.topk_ids, p.E)
+    assert np.array_equal(off_dev.cpu().numpy(), off)
+    SA_cpu = p.SA if layout == 0 else synth.to_m_major(p.SA)
+    C = _run(lib, d["A"], SA_cpu.cuda(), layout, d["B"], d["SB"], off_dev)
+    ref = grouped_gemm_bf16(p.A, SA_cpu.reshape(-1), layout, p.B, p.SB, off)
+    err = parity_error(bits_of(C), ref)
+    print(f"{name} layout={layout} R={p.R} parity_error={err:.3e}", flush=True)
+    assert err <= TOL
+    return bits_of(C)
+
+
+@pytest.mark.parametrize("name,layout", [
+    ("tiny", 0), ("tiny", 1),
+    ("decode_gateup", 0),
+    ("prefill_down", 0), ("prefill_down", 1),
+    ("e12_w13_m8", 0), ("e12_w13_m64", 0), ("e12_w2_m8", 0), ("e12_w2_m64", 0),
+    ("e12_w2_m64", 1),
+])
+def test_gemm_config_full(gpu_lib, name, layout):
+    _full_config(gpu_lib, name, layout)
+
+
+def test_gemm_prefill_gateup_sampled(gpu_lib):
+    """The 16384-token gate/up workload at full size, M-major scales; the
+    oracle recomputes sampled rows (expert and tile boundaries plus random
+    rows of every expert), all N columns each."""
+    p = synth.make_problem("prefill_gateup", device="cuda")
+    _, off_dev, _ = gpu_lib.route_prep(p.topk_ids.cuda(), p.E)
+    _, off, _ = route_ref(p.topk_ids, p.E)
+    assert np.array_equal(off_dev.cpu().numpy(), off)
+    SA_mm = synth.to_m_major(p.SA)
+    C = _run(gpu_lib, p.A, SA_mm, 1, p.B, p.SB, off_dev)
+    rng = np.random.default_rng(4)
+
+    def tile_m_of(rows):
+        cls, tm, _ = oplan.tile_rule(rows)
+        return tm if cls == oplan.CLASS_MFMA else 0
+
+    rows = sample_rows(off, tile_m_of, rng, per_expert_random=2)
+    ex = np.searchsorted(off, rows, side="right") - 1
+    rows_t = torch.from_numpy(rows).cuda()
+    a_rows = p.A[rows_t].cpu().numpy()
+    sa_r = sa_rows(SA_mm.cpu().numpy(), 1, rows, p.R, p.K)
+    Bc, SBc = p.B.cpu().numpy(), p.SB.cpu().numpy()
+    ref = bf16_rne_bits(rows_gemm_f64(a_rows, sa_r, ex, Bc, SBc))
+    got = bits_of(C[rows_t])
+    err = parity_error(got, ref)
+    print(f"prefill_gateup sampled rows={len(rows)} parity_error={err:.3e}", flush=True)
+    assert err <= TOL
+
+
+def _codes_case(lib, counts, N, K, seed, layout=0, exact=False, a_fill=None, sa_pow2=False):
+    A, SA, B, SB, off = synth.random_codes_problem(counts, N, K, seed)
+    R = int(off[-1])
+    if a_fill is not None:
+        A = a_fill(A)
+    if sa_pow2:
+        g = torch.Generator().manual_seed(seed + 1)
+        SA = torch.exp2(torch.randint(-3, 3, SA.shape, generator=g).float())
+    SA_l = SA if layout == 0 else synth.to_m_major(SA)
+    C = _run(lib, A.cuda(), SA_l.cuda(), layout, B.cuda(), SB.cuda(), off.cuda())
+    ref = grouped_gemm_bf16(A, SA_l.reshape(-1), layout, B, SB, off)
+    got = bits_of(C)
+    if exact:
+        assert np.array_equal(got, ref), int(np.sum(got != ref))
+    else:
+        err = parity_error(got, ref)
+        assert err <= TOL, err
+    return got
+
+
+MIXED = [0, 5, 64, 65, 130, 300, 17, 0, 128, 1, 257]
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_all_ones_bit_exact(gpu_lib, layout):
+    _A, _SA, B, SB, off = synth.random_codes_problem(MIXED, 288, 512, 7)
+    B = torch.full_like(B, 0x22)
+    R = int(off[-1])
+    g = torch.Generator().manual_seed(8)
+    SA = torch.exp2(torch.randint(-3, 3, (R, 4), generator=g).float())
+    A = torch.full((R, 512), 0x38, dtype=torch.uint8)
+    SA_l = SA if layout == 0 else synth.to_m_major(SA)
+    C = _run(gpu_lib, A.cuda(), SA_l.cuda(), layout, B.cuda(), SB.cuda(), off.cuda())
+    ref = grouped_gemm_bf16(A, SA_l.reshape(-1), layout, B, SB, off)
+    assert np.array_equal(bits_of(C), ref)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_one_hot_rows_bit_exact(gpu_lib, layout):
+    def one_hot(A):
+        g = torch.Generator().manual_seed(3)
+        R, K = A.shape
+        out = torch.zeros_like(A)
+        k0 = torch.randint(0, K, (R,), generator=g)
+        code = torch.randint(0, 0x7F, (R,), generator=g).to(torch.uint8) | \
+            (torch.randint(0, 2, (R,), generator=g).to(torch.uint8) << 7)
+        out[torch.arange(R), k0] = code
+        return out
+    _codes_case(gpu_lib, MIXED, 256, 384, 11, layout=layout, exact=True, a_fill=one_hot,
+                sa_pow2=True)
+
+
+def test_layouts_bit_identical_and_deterministic(gpu_lib):
+    a = _codes_case(gpu_lib, MIXED, 256, 640, 21, layout=0)
+    b = _codes_case(gpu_lib, MIXED, 256, 640, 21, layout=1)
+    c = _codes_case(gpu_lib, MIXED, 256, 640, 21, layout=0)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([3], 32, 128),                   # E = 1, one streaming item
+    ([200], 96, 256),                 # E = 1, MFMA class, partial n-tile
+    ([0, 0, 0, 70, 0], 288, 256),     # empty experts around one MFMA expert
+    ([64, 65, 16, 17, 48, 49], 320, 384),
+    (list(range(0, 140, 7)), 256, 128),
+])
+def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
+    _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
+
+
+def test_zero_rows(gpu_lib):
+    A, SA, B, SB, off = synth.random_codes_problem([0, 0, 0], 64, 256, 1)
+    # no rows at all: the binding has nothing to launch
+    C = gpu_lib.grouped_gemm(torch.zeros((0, 256), dtype=torch.uint8, device="cuda"),
+                             torch.zeros(0, dtype=torch.float32, device="cuda"), 0, B.cuda(),
+                             SB.cuda(), off.cuda())
+    assert C.shape == (0, 64)
+    # all experts empty on the device, with real buffers: the kernels write nothing
+    A1 = torch.zeros((1, 256), dtype=torch.uint8, device="cuda")
+    SA1 = torch.ones(2, dtype=torch.float32, device="cuda")
+    C1 = torch.full((1, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.grouped_gemm(A1, SA1, 0, B.cuda(), SB.cuda(), off.cuda(), out=C1)
+    torch.cuda.synchronize()
+    assert torch.all(C1 == 3.0)
+
+
+def test_bad_offsets_write_nothing(gpu_lib):
+    A, SA, B, SB, off = synth.random_codes_problem([10, 10, 10], 64, 256, 2)
+    bad = torch.tensor([0, 20, 10, 30], dtype=torch.int32)   # decreasing: rejected on device
+    C = torch.full((30, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    gpu_lib.grouped_gemm(A.cuda(), SA.cuda(), 0, B.cuda(), SB.cuda(), bad.cuda(), out=C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
