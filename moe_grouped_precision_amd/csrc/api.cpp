@@ -33,8 +33,7 @@ struct DeviceInfo {
   bool ready = false;
   bool supported = false;
   int cus = 0;
-  int grid_stream = 0;
-  int grid_mfma = 0;
+  int grid = 0;
 };
 
 constexpr int kMaxDevices = 64;
@@ -56,11 +55,10 @@ int device_info(const DeviceInfo** out) {
     d.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
     if (d.supported) {
-      int bs = 0, bm = 0;
-      e = w4a8::occupancy_blocks_per_cu(&bs, &bm);
+      int blocks = 0;
+      e = w4a8::occupancy_blocks_per_cu(&blocks);
       if (e != hipSuccess) return fail(W4A8_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
-      d.grid_stream = d.cus * (bs > 0 ? bs : 1);
-      d.grid_mfma = d.cus * (bm > 0 ? bm : 1);
+      d.grid = d.cus * (blocks > 0 ? blocks : 1);
     }
     d.ready = true;
   }
@@ -173,7 +171,7 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
   if (st != W4A8_OK) return st;
   w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev,
                       C_bf16_dev, E, N, K, a_scale_layout};
-  hipError_t e = w4a8::launch_grouped_gemm(args, d->grid_stream, d->grid_mfma, (hipStream_t)stream);
+  hipError_t e = w4a8::launch_grouped_gemm(args, d->grid, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,4 +1,4 @@
-// Grouped-contiguous W4A8 GEMM kernels for gfx950.
+// Grouped-contiguous W4A8 GEMM kernel for gfx950.
 //
 // C[r, n] = bf16( sum_g SA(r, g) * P_g[r, n] ),
 // P_g[r, n] = sum_{k in group g} e4m3(A[r, k]) * e2m1(B[e, n, k]) * 2^(SB[e, n, k/32] - 127)
@@ -22,13 +22,27 @@
 //   result        : lane holds rows-of-D 4q .. 4q+3 (= columns n) of column i
 //                   (= row m), i.e. four consecutive n of one output row.
 //
-// Two kernels share the plan rule of w4a8_device.h:
-//   gemm_stream_kernel  experts with <= S_MAX rows: weight streaming, one wave
-//                       per (expert, 32-column) item, fragments loaded straight
-//                       from global memory with a 4-deep prefetch ring (the
-//                       weights are read from HBM exactly once);
-//   gemm_mfma_kernel    larger experts: 256(n) x 128(m) workgroup tiles staged
-//                       through LDS (XOR-swizzled, double buffered).
+// One persistent launch of 512 threads (8 waves) per CU, two phases over the
+// tile plan of w4a8_device.h.  Both phases stream their operands through LDS
+// with direct global->LDS loads (global_load_lds_dwordx4 / _dword), which keep
+// no data in registers while in flight:
+//   * a 4-slot ring holds one K group of weights and activations per slot;
+//     every wave issues the same number of ring loads per stage, waits for
+//     the stage it needs with an explicit vmcnt and meets the others at one
+//     barrier per stage, so three stages are in flight at all times;
+//   * the E8M0 and activation scales are loaded four groups at a time (four
+//     lanes read 16 contiguous bytes) into a double buffer, so that they cost
+//     a small fraction of the memory requests of the weights;
+//   * the XOR swizzle that keeps fragment reads free of LDS bank conflicts is
+//     applied on the global-address side (a load lane always writes slot
+//     base + size * lane).
+// Phases:
+//   1. streaming items (experts with <= S_MAX rows): one workgroup per
+//      (expert, 64 or 128 columns); waves 0-3 take the first half of the K
+//      groups and waves 4-7 the second half, each wave 16 or 32 columns; the
+//      halves are added in LDS (always half 0 + half 1) before the bf16 store.
+//   2. MFMA tiles (larger experts): 256(n) x 128(m) per workgroup, one K group
+//      per stage; each wave owns 64(n) x 64(m).
 #include "w4a8_device.h"
 #include "w4a8_launch.h"
 
@@ -37,6 +51,53 @@ namespace w4a8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BLOCK = 512;
+constexpr int WAVES = BLOCK / 64;
+constexpr int NS = 4;                  // ring slots (NS-1 stages in flight)
+constexpr int SLOT_BYTES = 32768;      // one K group: weights 16 KB + activations 16 KB
+constexpr int SLOT_X = 0;              // activation rows
+constexpr int SLOT_W = 16384;          // weight columns
+constexpr int SC = 4;                  // groups per scale chunk
+constexpr int SB_BYTES = 4096;         // one scale chunk of E8M0 codes (1024 x u32)
+constexpr int SA_BYTES = 2048;         // one scale chunk of activation scales (512 x fp32)
+constexpr int LDS_SB = NS * SLOT_BYTES;          // 2 buffers
+constexpr int LDS_SA = LDS_SB + 2 * SB_BYTES;    // 2 buffers
+constexpr int LDS_BYTES = LDS_SA + 2 * SA_BYTES;
+
+#define W4A8_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define W4A8_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Each active lane copies 16 (or 4) bytes from its own global address to
+// lds_wave_base + 16 * lane (or 4 * lane).  lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(W4A8_GPTR(g), W4A8_LPTR(lds_wave_base), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(W4A8_GPTR(g), W4A8_LPTR(lds_wave_base), 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `pending` later stages of PER_STAGE ring loads each are
+// still in flight, then meet the other waves.  Scale-chunk loads issued with a
+// later stage only make this wait stricter than needed, never looser.
+template <int PER_STAGE>
+__device__ __forceinline__ void stage_barrier(int pending) {
+  static_assert((NS - 2) * PER_STAGE < 64, "too many loads in flight");
+  if (pending >= 2) wait_vm<2 * PER_STAGE>();
+  else if (pending == 1) wait_vm<PER_STAGE>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ v4f mfma_group(v4i w, v4i x_lo, v4i x_hi, int sb) {
   v8i a = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
@@ -60,313 +121,371 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v) {
   *reinterpret_cast<uint2*>(dst) = o;
 }
 
+__device__ __forceinline__ v4i lds128(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+__device__ __forceinline__ uint32_t lds32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ float ldsf(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
+
+// Activation scale of (row, group) in either layout.
+__device__ __forceinline__ const float* sa_ptr(const GemmArgs& p, size_t row, int g, int G, int R) {
+  return p.layout == 0 ? p.SA + row * (size_t)G + g : p.SA + (size_t)g * R + row;
+}
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel (small experts)
+// Phase 1: weight streaming (experts with <= S_MAX rows)
+//
+// Stage s covers group gb[h] + s of each K half h (gb = {0, ceil(G/2)}).
+// Ring slot:  X [2 halves][16*mb rows][128 B] @ SLOT_X   (row chunk c at c ^ (row & 7))
+//             W [8 waves][NBW][16 cols][64 B] @ SLOT_W   (col chunk c at c ^ ((col >> 1) & 3))
+// Scale chunk c (stages SC*c .. SC*c+3):
+//             SB [2 halves][128 cols][SC] u32;  SA [2 halves][64 rows][SC] fp32
 // ---------------------------------------------------------------------------
-constexpr int STREAM_DEPTH = 4;
+template <int NBW>
+struct StreamItem {
+  static constexpr int WIDTH = 4 * NBW * 16;  // columns per item
 
-template <int MB>
-struct StreamStage {
-  v4i w[2];
-  int s[2];
-  v4i x[MB][2];
-  float a[MB];
+  // Ring loads of stage s: NBW (W) + mb (X) per wave.
+  __device__ __forceinline__ static void issue_stage(const GemmArgs& p, uint8_t* slot, int e,
+                                                     int row0, int rows, int mb, int n0, int s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kh = wave >> 2, wn = wave & 3;
+    const int K = p.K, N = p.N, G = K >> 7;
+    const int g0 = min(s, G - 1), g1 = min((G + 1) / 2 + s, G - 1);  // group of each K half
+    const int gk = kh ? g1 : g0;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {  // 16 cols x 64 B
+      const int r = lane >> 2;
+      const int c = (lane & 3) ^ ((r >> 1) & 3);
+      const int n = min(n0 + (wn * NBW + j) * 16 + r, N - 1);
+      dma16(p.B + ((size_t)e * N + n) * (size_t)(K >> 1) + (size_t)gk * 64 + c * 16,
+            slot + SLOT_W + (wave * NBW + j) * 1024);
+    }
+    for (int i = 0; i < mb; ++i) {  // 8*mb loads of 4 rows x 128 B
+      if (lane < 32) {
+        const int jx = wave * mb + i;
+        const int h = jx / (4 * mb), quad = jx - h * (4 * mb);
+        const int r = quad * 4 + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const size_t row = (size_t)row0 + min(r, rows - 1);
+        dma16(p.A + row * (size_t)K + (size_t)(h ? g1 : g0) * 128 + c * 16,
+              slot + SLOT_X + h * (mb * 16 * 128) + quad * 512);
+      }
+    }
+  }
+
+  // Scale chunk c: 2 SB + 1 SA loads per wave.
+  __device__ __forceinline__ static void issue_scales(const GemmArgs& p, uint8_t* lds, int e,
+                                                      int row0, int rows, int n0, int c, int R) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = p.K, N = p.N, G = K >> 7;
+    const int gb1 = (G + 1) / 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = (wave * 2 + i) * 64 + lane;  // [h][col][gg]
+      const int h = idx >> 9, col = (idx >> 2) & 127, gg = idx & 3;
+      const int n = min(n0 + col, N - 1);
+      const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
+      dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+           lds + LDS_SB + (c & 1) * SB_BYTES + (wave * 2 + i) * 256);
+    }
+    {
+      const int idx = wave * 64 + lane;  // [h][row][gg]
+      const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
+      const size_t row = (size_t)row0 + min(r, rows - 1);
+      const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
+      dma4(sa_ptr(p, row, g, G, R), lds + LDS_SA + (c & 1) * SA_BYTES + wave * 256);
+    }
+  }
+
+  __device__ __forceinline__ static void run(const GemmArgs& p, uint8_t* lds, int e, int row0,
+                                             int rows, int n0, int R) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kh = wave >> 2, wn = wave & 3;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int G = p.K >> 7;
+    const int Gh = (G + 1) / 2;
+    const int gcount = kh == 0 ? Gh : G - Gh;  // groups of this wave's half
+    const int S = Gh;
+    const int mb = (rows + 15) >> 4;             // 1..4 row blocks
+
+    v4f acc[NBW][4];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    wait_vm<0>();  // earlier stores must not be counted against this item's loads
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+      if (s < S) {
+        if (s % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s / SC, R);
+        issue_stage(p, lds + s * SLOT_BYTES, e, row0, rows, mb, n0, s);
+      }
+    }
+
+    for (int s = 0; s < S; ++s) {
+      switch (mb) {
+        case 1: stage_barrier<NBW + 1>(min(NS - 2, S - 1 - s)); break;
+        case 2: stage_barrier<NBW + 2>(min(NS - 2, S - 1 - s)); break;
+        case 3: stage_barrier<NBW + 3>(min(NS - 2, S - 1 - s)); break;
+        default: stage_barrier<NBW + 4>(min(NS - 2, S - 1 - s)); break;
+      }
+      const int sn = s + NS - 1;
+      if (sn < S) {
+        if (sn % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn / SC, R);
+        issue_stage(p, lds + (sn % NS) * SLOT_BYTES, e, row0, rows, mb, n0, sn);
+      }
+      if (s < gcount) {
+        const uint8_t* slot = lds + (s % NS) * SLOT_BYTES;
+        const uint8_t* sbb = lds + LDS_SB + ((s / SC) & 1) * SB_BYTES;
+        const uint8_t* sab = lds + LDS_SA + ((s / SC) & 1) * SA_BYTES;
+        const int gg = s % SC;
+        v4i wf[NBW];
+        int sbv[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const int col = (wn * NBW + j) * 16 + r16;
+          wf[j] = lds128(slot + SLOT_W + (wave * NBW + j) * 1024 + r16 * 64 + ((q ^ ((r16 >> 1) & 3)) << 4));
+          sbv[j] = (int)((lds32(sbb + ((kh * 128 + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < mb) {
+            const int m = i * 16 + r16;
+            const uint8_t* xb = slot + SLOT_X + kh * (mb * 16 * 128) + m * 128;
+            const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
+            const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
+            const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) promote(acc[j][i], sa, mfma_group(wf[j], x0, x1, sbv[j]));
+          }
+        }
+      }
+    }
+
+    // add the two K halves in LDS (the ring is free: every wave passed the last
+    // stage barrier with nothing in flight) and store
+    __syncthreads();
+    v4f* red = reinterpret_cast<v4f*>(lds);
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < mb) red[((wn * NBW + j) * 4 + i) * 64 + lane] = acc[j][i];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 16 + r16;
+        if (i < mb && m < rows) {
+          uint16_t* crow = p.C + (size_t)(row0 + m) * p.N;
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int n = n0 + (wn * NBW + j) * 16 + q * 4;
+            const v4f o = red[((wn * NBW + j) * 4 + i) * 64 + lane];
+            if (n < p.N) store_bf16x4(crow + n, acc[j][i] + o);
+          }
+        }
+      }
+    }
+    __syncthreads();  // red is overwritten by the next item's loads
+  }
 };
 
-template <int MB>
-__device__ void stream_item(const GemmArgs& p, int e, int row0, int rows, int n0, int R) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, r16 = lane & 15;
-  const int K = p.K, N = p.N;
-  const int G = K >> 7;
-
-  const uint8_t* wp[2];
-  const uint8_t* sp[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const size_t col = (size_t)e * N + n0 + j * 16 + r16;
-    wp[j] = p.B + col * (size_t)(K >> 1) + q * 16;
-    sp[j] = p.SB + col * (size_t)(K >> 5) + q;
-  }
-  const uint8_t* xp[MB];
-  const float* ap[MB];
-  bool xv[MB];
-  const size_t astride = p.layout == 0 ? 1 : (size_t)R;
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = i * 16 + r16;
-    xv[i] = m < rows;
-    const size_t row = (size_t)row0 + (xv[i] ? m : 0);
-    xp[i] = p.A + row * (size_t)K + q * 16;
-    ap[i] = p.layout == 0 ? p.SA + row * (size_t)G : p.SA + row;
-  }
-
-  StreamStage<MB> st[STREAM_DEPTH];
-  auto load = [&](StreamStage<MB>& S, int g) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      S.w[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp[j] + (size_t)g * 64));
-      S.s[j] = sp[j][g * 4];
-    }
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      if (xv[i]) {
-        const uint8_t* src = xp[i] + (size_t)g * 128;
-        S.x[i][0] = *reinterpret_cast<const v4i*>(src);
-        S.x[i][1] = *reinterpret_cast<const v4i*>(src + 64);
-        S.a[i] = ap[i][(size_t)g * astride];
-      } else {
-        S.x[i][0] = v4i{0, 0, 0, 0};
-        S.x[i][1] = v4i{0, 0, 0, 0};
-        S.a[i] = 0.f;
-      }
-    }
-  };
-
-  v4f acc[2][MB];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < STREAM_DEPTH; ++s)
-    if (s < G) load(st[s], s);
-
-  for (int g0 = 0; g0 < G; g0 += STREAM_DEPTH) {
-#pragma unroll
-    for (int s = 0; s < STREAM_DEPTH; ++s) {
-      const int g = g0 + s;
-      if (g < G) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-            promote(acc[j][i], st[s].a[i], mfma_group(st[s].w[j], st[s].x[i][0], st[s].x[i][1], st[s].s[j]));
-        if (g + STREAM_DEPTH < G) load(st[s], g + STREAM_DEPTH);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = i * 16 + r16;
-    if (m < rows) {
-      uint16_t* crow = p.C + (size_t)(row0 + m) * N + n0 + q * 4;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) store_bf16x4(crow + j * 16, acc[j][i]);
-    }
-  }
-}
-
-__global__ void __launch_bounds__(256)
-gemm_stream_kernel(GemmArgs p) {
-  __shared__ int s_off[MAX_EXPERTS + 1];
-  __shared__ int s_base[MAX_EXPERTS + 1];
-  __shared__ int s_wave[4];
-  if (!plan_prologue(p.offsets, p.E, CLASS_STREAM, s_off, s_base, s_wave)) return;
-  const int tiles = s_base[p.E];
-  const int nb = p.N / TN_STREAM;
-  const long long items = (long long)tiles * nb;
-  const long long nw = (long long)gridDim.x * (blockDim.x >> 6);
-  const int R = s_off[p.E];
-  for (long long it = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); it < items;
-       it += nw) {
-    const int mt = (int)(it / nb);
-    const int n0 = (int)(it % nb) * TN_STREAM;
-    const int e = expert_of_tile(s_base, p.E, mt);
-    const int row0 = s_off[e];
-    const int rows = s_off[e + 1] - row0;
-    switch ((rows + 15) >> 4) {
-      case 1: stream_item<1>(p, e, row0, rows, n0, R); break;
-      case 2: stream_item<2>(p, e, row0, rows, n0, R); break;
-      case 3: stream_item<3>(p, e, row0, rows, n0, R); break;
-      default: stream_item<4>(p, e, row0, rows, n0, R); break;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// MFMA kernel (larger experts): 256(n) x 128(m) tiles through LDS
+// Phase 2: MFMA tiles (larger experts), 256(n) x 128(m), one group per stage.
+// Ring slot:  X [128 rows][128 B] @ SLOT_X   (row chunk c at c ^ (row & 7))
+//             W [256 cols][64 B]  @ SLOT_W   (col chunk c at c ^ ((col >> 1) & 3))
+// Scale chunk c (groups SC*c .. SC*c+3):  SB [256 cols][SC] u32;  SA [128 rows][SC] fp32
 // ---------------------------------------------------------------------------
 constexpr int MF_BN = TN_MFMA;  // 256 weight columns
 constexpr int MF_BM = T_MAX;    // 128 activation rows
+constexpr int P2_PER_STAGE = 4; // W 2, X 2 ring loads per wave
 
-struct MfStage {
-  uint8_t w[MF_BN * 64];   // [n][64 B]  16-B chunks XOR-swizzled by (n >> 1) & 3
-  uint8_t x[MF_BM * 128];  // [m][128 B] 16-B chunks XOR-swizzled by m & 7
-  uint32_t sb[MF_BN];      // the 4 E8M0 codes of this group, per column
-  float sa[MF_BM];         // activation scale of this group, per row
-};
-
-__device__ __forceinline__ int w_off(int n, int ch) { return n * 64 + ((ch ^ ((n >> 1) & 3)) << 4); }
-__device__ __forceinline__ int x_off(int m, int ch) { return m * 128 + ((ch ^ (m & 7)) << 4); }
-
-struct MfRegs {
-  v4i w[4];
-  v4i x[4];
-  uint32_t sb;
-  float sa;
-};
-
-__device__ __forceinline__ void mf_load(const GemmArgs& p, MfRegs& r, int e, int row0, int rows,
-                                        int n0, int g, int R) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void mf_issue_stage(const GemmArgs& p, uint8_t* slot, int e, int row0,
+                                               int rows, int n0, int g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K, N = p.N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int n = c >> 2, ch = c & 3;
-    if (n0 + n < N) {
-      const uint8_t* src = p.B + ((size_t)e * N + n0 + n) * (size_t)(K >> 1) + (size_t)g * 64 + ch * 16;
-      r.w[i] = *reinterpret_cast<const v4i*>(src);
-    } else {
-      r.w[i] = v4i{0, 0, 0, 0};
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave * 2 + i;  // 16 columns x 64 B
+    const int r = j * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 1) & 3);
+    const int n = min(n0 + r, N - 1);
+    dma16(p.B + ((size_t)e * N + n) * (size_t)(K >> 1) + (size_t)g * 64 + c * 16, slot + SLOT_W + j * 1024);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int m = c >> 3, ch = c & 7;
-    if (m < rows) {
-      const uint8_t* src = p.A + (size_t)(row0 + m) * (size_t)K + (size_t)g * 128 + ch * 16;
-      r.x[i] = *reinterpret_cast<const v4i*>(src);
-    } else {
-      r.x[i] = v4i{0, 0, 0, 0};
-    }
-  }
-  {
-    const int n = tid;
-    r.sb = (n0 + n < N)
-               ? *reinterpret_cast<const uint32_t*>(p.SB + ((size_t)e * N + n0 + n) * (size_t)(K >> 5) + g * 4)
-               : 0x7f7f7f7fu;
-  }
-  {
-    const int m = tid;
-    float s = 0.f;
-    if (m < MF_BM && m < rows) {
-      const size_t row = (size_t)row0 + m;
-      s = p.layout == 0 ? p.SA[row * (size_t)(K >> 7) + g] : p.SA[(size_t)g * R + row];
-    }
-    r.sa = s;
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave * 2 + i;  // 8 rows x 128 B
+    const int r = j * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    const size_t row = (size_t)row0 + min(r, rows - 1);
+    dma16(p.A + row * (size_t)K + (size_t)g * 128 + c * 16, slot + SLOT_X + j * 1024);
   }
 }
 
-__device__ __forceinline__ void mf_store(MfStage& s, const MfRegs& r) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void mf_issue_scales(const GemmArgs& p, uint8_t* lds, int e, int row0,
+                                                int rows, int n0, int c, int R) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K, N = p.N, G = K >> 7;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    *reinterpret_cast<v4i*>(s.w + w_off(c >> 2, c & 3)) = r.w[i];
+  for (int i = 0; i < 2; ++i) {
+    const int idx = (wave * 2 + i) * 64 + lane;  // [col][gg]
+    const int col = idx >> 2, gg = idx & 3;
+    const int n = min(n0 + col, N - 1);
+    const int g = min(SC * c + gg, G - 1);
+    dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+         lds + LDS_SB + (c & 1) * SB_BYTES + (wave * 2 + i) * 256);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    *reinterpret_cast<v4i*>(s.x + x_off(c >> 3, c & 7)) = r.x[i];
+  {
+    const int idx = wave * 64 + lane;  // [row][gg]
+    const int r = idx >> 2, gg = idx & 3;
+    const size_t row = (size_t)row0 + min(r, rows - 1);
+    const int g = min(SC * c + gg, G - 1);
+    dma4(sa_ptr(p, row, g, G, R), lds + LDS_SA + (c & 1) * SA_BYTES + wave * 256);
   }
-  s.sb[tid] = r.sb;
-  if (tid < MF_BM) s.sa[tid] = r.sa;
 }
 
-__device__ void mfma_tile(const GemmArgs& p, MfStage* stg, int e, int row0, int rows, int n0, int R) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+__device__ __forceinline__ void mfma_tile(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
+                                          int n0, int R) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave & 3, wm = wave >> 2;  // 4 waves along n (64 each), 2 along m
   const int q = lane >> 4, r16 = lane & 15;
   const int G = p.K >> 7;
+  // row blocks of this wave that hold real rows: wm, wm+2, wm+4, wm+6
+  const int nmb = uniform(rows > wm * 16 ? min(4, (rows - wm * 16 + 31) / 32) : 0);
 
-  v4f acc[4][8];
+  v4f acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  MfRegs r;
-  mf_load(p, r, e, row0, rows, n0, 0, R);
-  mf_store(stg[0], r);
-  __syncthreads();
+  wait_vm<0>();
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    if (s < G) {
+      if (s % SC == 0) mf_issue_scales(p, lds, e, row0, rows, n0, s / SC, R);
+      mf_issue_stage(p, lds + s * SLOT_BYTES, e, row0, rows, n0, s);
+    }
+  }
 
   for (int g = 0; g < G; ++g) {
-    const int cur = g & 1;
-    if (g + 1 < G) mf_load(p, r, e, row0, rows, n0, g + 1, R);
-    const MfStage& s = stg[cur];
-    v4i wf[8];
-    int sbv[8];
+    stage_barrier<P2_PER_STAGE>(min(NS - 2, G - 1 - g));
+    const int gn = g + NS - 1;
+    if (gn < G) {
+      if (gn % SC == 0) mf_issue_scales(p, lds, e, row0, rows, n0, gn / SC, R);
+      mf_issue_stage(p, lds + (gn % NS) * SLOT_BYTES, e, row0, rows, n0, gn);
+    }
+    const uint8_t* slot = lds + (g % NS) * SLOT_BYTES;
+    const uint8_t* sbb = lds + LDS_SB + ((g / SC) & 1) * SB_BYTES;
+    const uint8_t* sab = lds + LDS_SA + ((g / SC) & 1) * SA_BYTES;
+    const int gg = g % SC;
+    v4i wf[4];
+    int sbv[4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const int n = wn * 128 + nb * 16 + r16;
-      wf[nb] = *reinterpret_cast<const v4i*>(s.w + w_off(n, q));
-      sbv[nb] = (int)((s.sb[n] >> (8 * q)) & 0xffu);
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = wn * 64 + nb * 16 + r16;
+      wf[nb] = lds128(slot + SLOT_W + n * 64 + ((q ^ ((n >> 1) & 3)) << 4));
+      sbv[nb] = (int)((lds32(sbb + (n * SC + gg) * 4) >> (8 * q)) & 0xffu);
+    }
+    v4i x0[4], x1[4];
+    float sa[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int m = (wm + 2 * mi) * 16 + r16;
+      const uint8_t* xb = slot + SLOT_X + m * 128;
+      x0[mi] = lds128(xb + ((q ^ (m & 7)) << 4));
+      x1[mi] = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
+      sa[mi] = ldsf(sab + (m * SC + gg) * 4);
     }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const int mb = wm + 2 * mi;
-      if (mb * 16 < rows) {
-        const int m = mb * 16 + r16;
-        const v4i x0 = *reinterpret_cast<const v4i*>(s.x + x_off(m, q));
-        const v4i x1 = *reinterpret_cast<const v4i*>(s.x + x_off(m, q + 4));
-        const float sa = s.sa[m];
+      if (mi < nmb) {
+        v4f pr[4];
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) promote(acc[mi][nb], sa, mfma_group(wf[nb], x0, x1, sbv[nb]));
+        for (int nb = 0; nb < 4; ++nb) pr[nb] = mfma_group(wf[nb], x0[mi], x1[mi], sbv[nb]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) promote(acc[mi][nb], sa[mi], pr[nb]);
       }
     }
-    if (g + 1 < G) mf_store(stg[cur ^ 1], r);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the ring before the next tile's loads
 
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    const int mb = wm + 2 * mi;
-    const int m = mb * 16 + r16;
+    const int m = (wm + 2 * mi) * 16 + r16;
     if (m < rows) {
       uint16_t* crow = p.C + (size_t)(row0 + m) * p.N;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int n = n0 + wn * 128 + nb * 16 + q * 4;
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = n0 + wn * 64 + nb * 16 + q * 4;
         if (n < p.N) store_bf16x4(crow + n, acc[mi][nb]);
       }
     }
   }
 }
 
-__global__ void __launch_bounds__(256)
-gemm_mfma_kernel(GemmArgs p) {
-  __shared__ MfStage stg[2];
+// ---------------------------------------------------------------------------
+// The kernel: plan prologue, then both phases.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(BLOCK, 1)
+grouped_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int s_off[MAX_EXPERTS + 1];
-  __shared__ int s_base[MAX_EXPERTS + 1];
-  __shared__ int s_wave[4];
-  if (!plan_prologue(p.offsets, p.E, CLASS_MFMA, s_off, s_base, s_wave)) return;
-  const int tiles = s_base[p.E];
-  const int nt_count = (p.N + MF_BN - 1) / MF_BN;
-  const long long items = (long long)tiles * nt_count;
-  const int R = s_off[p.E];
-  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-    const int mt = (int)(it / nt_count);
-    const int n0 = (int)(it % nt_count) * MF_BN;
-    const int e = expert_of_tile(s_base, p.E, mt);
-    const int j = mt - s_base[e];
-    const int rows_e = s_off[e + 1] - s_off[e];
-    const TileChoice tc = tile_rule(rows_e);
-    const int row0 = s_off[e] + j * tc.tile_m;
-    const int rows = min(tc.tile_m, rows_e - j * tc.tile_m);
-    mfma_tile(p, stg, e, row0, rows, n0, R);
+  __shared__ int s_sbase[MAX_EXPERTS + 1];
+  __shared__ int s_mbase[MAX_EXPERTS + 1];
+  __shared__ int s_wave[WAVES];
+  if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_wave)) return;
+  const int R = uniform(s_off[p.E]);
+
+  // phase 1: streaming items, one workgroup each.  Items are 128 columns wide
+  // when that still gives every workgroup three or more items, else 64.
+  {
+    const int tiles = uniform(s_sbase[p.E]);
+    const long long items128 = (long long)tiles * ((p.N + 127) / 128);
+    const bool wide = items128 >= 3LL * gridDim.x;
+    const int width = wide ? StreamItem<2>::WIDTH : StreamItem<1>::WIDTH;
+    const int nchunks = (p.N + width - 1) / width;
+    const long long items = (long long)tiles * nchunks;
+    for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+      const int mt = (int)(it / nchunks);
+      const int n0 = (int)(it % nchunks) * width;
+      const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
+      const int row0 = uniform(s_off[e]);
+      const int rows = uniform(s_off[e + 1]) - row0;
+      if (wide) StreamItem<2>::run(p, lds, e, row0, rows, n0, R);
+      else StreamItem<1>::run(p, lds, e, row0, rows, n0, R);
+    }
+  }
+
+  // phase 2: MFMA tiles, one workgroup each
+  {
+    const int nt_count = (p.N + MF_BN - 1) / MF_BN;
+    const long long items = (long long)uniform(s_mbase[p.E]) * nt_count;
+    for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+      const int mt = (int)(it / nt_count);
+      const int n0 = (int)(it % nt_count) * MF_BN;
+      const int e = uniform(expert_of_tile(s_mbase, p.E, mt));
+      const int j = mt - uniform(s_mbase[e]);
+      const int base = uniform(s_off[e]);
+      const int rows_e = uniform(s_off[e + 1]) - base;
+      const TileChoice tc = tile_rule(rows_e);
+      const int row0 = base + j * tc.tile_m;
+      const int rows = min(tc.tile_m, rows_e - j * tc.tile_m);
+      mfma_tile(p, lds, e, row0, rows, n0, R);
+    }
   }
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& args, int grid_stream, int grid_mfma,
-                               hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_stream_kernel, dim3(grid_stream), dim3(256), 0, stream, args);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_mfma_kernel, dim3(grid_mfma), dim3(256), 0, stream, args);
+hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_gemm_kernel, dim3(grid), dim3(BLOCK), 0, stream, args);
   return hipGetLastError();
 }
 
-hipError_t occupancy_blocks_per_cu(int* stream_blocks, int* mfma_blocks) {
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(stream_blocks, gemm_stream_kernel, 256, 0);
-  if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(mfma_blocks, gemm_mfma_kernel, 256, 0);
+hipError_t occupancy_blocks_per_cu(int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, grouped_gemm_kernel, BLOCK, 0);
 }
 
 }  // namespace w4a8

@@ -104,13 +104,14 @@ __device__ inline uint32_t bf16_rne(float f) {
 
 // ---------------------------------------------------------------------------
 // Plan prologue run by every GEMM workgroup: offsets into LDS, validity check,
-// and the exclusive scan of the m-tile counts of one class.
-//   s_off[0..E]   expert offsets
-//   s_base[0..E]  first m-tile of each expert within the class; s_base[E] = total
+// and the exclusive scans of the m-tile counts of both classes.
+//   s_off[0..E]    expert offsets
+//   s_sbase[0..E]  first streaming-class m-tile of each expert; [E] = total
+//   s_mbase[0..E]  first MFMA-class m-tile of each expert;      [E] = total
 // Returns false (uniformly across the block) if the offsets are invalid.
 // ---------------------------------------------------------------------------
-__device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int cls,
-                                     int* s_off, int* s_base, int* s_wave) {
+__device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int* s_off,
+                                     int* s_sbase, int* s_mbase, int* s_wave) {
   const int tid = threadIdx.x;
   for (int i = tid; i <= E; i += blockDim.x) s_off[i] = offsets[i];
   __syncthreads();
@@ -122,25 +123,32 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
   // each thread owns a contiguous run of experts
   const int per = (E + blockDim.x - 1) / blockDim.x;
   const int e0 = tid * per;
-  int local = 0;
+  int ls = 0, lm = 0;
   for (int i = 0; i < per; ++i) {
     int e = e0 + i;
     if (e < E) {
       TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
-      local += (t.cls == cls) ? t.n_m : 0;
+      ls += (t.cls == CLASS_STREAM) ? t.n_m : 0;
+      lm += (t.cls == CLASS_MFMA) ? t.n_m : 0;
     }
   }
-  int total;
-  int run = block_exclusive_scan(local, s_wave, &total);
+  int tot_s, tot_m;
+  int rs = block_exclusive_scan(ls, s_wave, &tot_s);
+  int rm = block_exclusive_scan(lm, s_wave, &tot_m);
   for (int i = 0; i < per; ++i) {
     int e = e0 + i;
     if (e < E) {
-      s_base[e] = run;
+      s_sbase[e] = rs;
+      s_mbase[e] = rm;
       TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
-      run += (t.cls == cls) ? t.n_m : 0;
+      rs += (t.cls == CLASS_STREAM) ? t.n_m : 0;
+      rm += (t.cls == CLASS_MFMA) ? t.n_m : 0;
     }
   }
-  if (tid == 0) s_base[E] = total;
+  if (tid == 0) {
+    s_sbase[E] = tot_s;
+    s_mbase[E] = tot_m;
+  }
   __syncthreads();
   return true;
 }

@@ -21,8 +21,7 @@ hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts, 
                              int32_t* row_of_slot, hipStream_t stream);
 hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int max_tiles,
                        hipStream_t stream);
-hipError_t launch_grouped_gemm(const GemmArgs& args, int grid_stream, int grid_mfma,
-                               hipStream_t stream);
-hipError_t occupancy_blocks_per_cu(int* stream_blocks, int* mfma_blocks);
+hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream);
+hipError_t occupancy_blocks_per_cu(int* blocks);
 
 }  // namespace w4a8
