@@ -7,7 +7,7 @@ batch of seeded synthetic inputs already resident in HBM.
     python bench.py [--steps K] [--warmup W] [--config NAME] [--layout 0|1]
 
 Prints one JSON line.  value = whole-step TFLOP/s (2*R*N*K per step);
-roofline = the grouped GEMM launch (both kernel classes, one call) against
+roofline = the grouped GEMM kernel launch against
 HBM (8 TB/s) or the FP8-rate MFMA peak (5.0 PFLOP/s); cpu_baseline = the
 CPU oracle timed on a bounded sample of the same workload.
 """
@@ -15,9 +15,11 @@ CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -34,8 +36,48 @@ DEFAULT_STEPS = {"prefill_gateup": 20}
 BOUND = {"prefill_gateup": "mfma", "prefill_down": "mfma"}
 
 
+KERNEL_SOURCES = ("moe_grouped_precision_amd/csrc/gemm.hip", "moe_grouped_precision_amd/csrc/w4a8_device.h")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name: str, layout: int):
+    """HBM bytes per launch recorded from rocprofv3 counters for this exact
+    kernel source (profiles/traffic_<workload>.md); None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_layout{layout}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_bytes.group(1))
+
+
+def copy_calibration(steps: int):
+    """A plain 1 GiB device copy, for scaling the memory counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": steps}), flush=True)
 
 
 def algorithmic_bytes(counts, E, N, K):
@@ -95,12 +137,18 @@ def main():
     ap.add_argument("--layout", type=int, default=None, help="0 row-major, 1 M-major input scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU component)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps or 5)
+        return
 
     import numpy as np
     import torch
@@ -176,11 +224,12 @@ def main():
     if bound == "hbm":
         achieved = nbytes / (gemm_med * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(name, layout)}
     else:
         achieved = flops / (gemm_med * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFS, 4),
+                "traffic": recorded_traffic(name, layout)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -212,6 +261,7 @@ def main():
             "algorithmic_bytes": int(nbytes),
             "flop": flops,
             "weight_copies_rotated": nrot,
+            "kernel_source_sha256": kernel_source_hash(),
         },
         "roofline": roof,
         "cpu_baseline": cpu,
