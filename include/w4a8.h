@@ -66,6 +66,7 @@ enum {
 
 /* Limits of this version. */
 #define W4A8_MAX_EXPERTS 1024
+#define W4A8_MAX_K 1048576     /* keeps every in-tile byte offset within 32 bits */
 
 /*
  * w4a8_route_prep -- routing histogram, exclusive-scan offsets and row map.
@@ -132,8 +133,8 @@ int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K,
  * expert_offsets_dev int32 [E+1], offsets[0] = 0, nondecreasing.
  * C_bf16_dev         out uint16 (bf16 bits) [R][N]; only rows < R are written.
  *                    16-byte aligned.
- * Limits: 1 <= E <= W4A8_MAX_EXPERTS; K % 128 == 0, K >= 128; N % 32 == 0,
- * N >= 32; R*K and R*N below 2^62.  A, a_scales and C must hold R rows.
+ * Limits: 1 <= E <= W4A8_MAX_EXPERTS; K % 128 == 0, 128 <= K <= W4A8_MAX_K;
+ * N % 32 == 0, N >= 32; R*K and R*N below 2^62.  A, a_scales and C must hold R rows.
  * Numerics: each 128-K group is reduced by a scaled MFMA in fp32 (E8M0 weight
  * scales applied inside it), multiplied by its fp32 activation scale and
  * accumulated in fp32; one RNE rounding to bf16 at the end.  NaN codes
@@ -146,8 +147,8 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
 
 /*
  * w4a8_plan_params -- the plan rule's constants, written to out_host[0..n-1]
- * in this order: GRAN (m granularity), S_MAX, T_MAX, TN_STREAM (n width of a
- * streaming work item), TN_MFMA (n width of an MFMA work item), plan header
+ * in this order: GRAN (m granularity), S_MAX, T_MAX, TN_STREAM (n granularity
+ * of streaming work), TN_MFMA (n width of an MFMA work item), plan header
  * words, words per tile.  Returns the number of constants available (7) or
  * -W4A8_ERR_NULL if out_host is NULL.
  */

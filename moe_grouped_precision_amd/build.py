@@ -39,6 +39,10 @@ def compile_flags(debug: bool = False):
         "-I", os.path.join(ROOT, "include"),
         "-I", CSRC,
         "-Wall",
+        # the K-loop asm names m0 (the LDS base of direct-to-LDS loads) as
+        # clobbered; the compiler notes that it does not preserve m0, which is
+        # what the kernels expect
+        "-Wno-inline-asm",
     ]
     flags += ["-O0", "-g"] if debug else ["-O3"]
     return flags

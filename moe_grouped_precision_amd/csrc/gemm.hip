@@ -31,14 +31,16 @@
 //      registers (a per-wave ring two stages deep); the activation rows and
 //      the scales are shared through LDS.  The halves are added in LDS
 //      (always half 0 + half 1) before the bf16 store.
-//   2. MFMA tiles (larger experts): 256(n) x 128(m) per workgroup, one K group
-//      per stage through a 4-slot LDS ring (three stages in flight); each
-//      wave owns 64(n) x 64(m).
+//   2. MFMA tiles (larger experts): 512(n) x 128(m) per workgroup, one K group
+//      per stage; each wave owns 64 columns x all 128 rows, its weights in a
+//      register ring, the activation rows in a 4-slot LDS ring (three stages
+//      in flight); tiles are dealt so that each XCD works on a compact block.
 // Shared operands reach LDS through direct global->LDS loads
 // (global_load_lds_dwordx4 / _dword), which hold no registers while in
 // flight: every wave issues the same number of loads per stage, waits for the
-// stage it needs with an explicit vmcnt and meets the others at one barrier
-// per stage.  The E8M0 and activation scales are loaded four groups at a time
+// stage it needs with one explicit vmcnt and meets the others at one barrier
+// per stage.  All vector-memory ops of the K loops are inline asm (see the
+// helpers below for why).  The E8M0 and activation scales are loaded four groups at a time
 // (four lanes read 16 contiguous bytes) into a double buffer, so they cost a
 // small fraction of the memory requests of the weights.  The XOR swizzle that
 // keeps fragment reads free of LDS bank conflicts is applied on the
@@ -48,7 +50,6 @@
 #include "w4a8_device.h"
 #include "w4a8_launch.h"
 
-
 namespace w4a8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -57,48 +58,85 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BLOCK = 512;
 constexpr int WAVES = BLOCK / 64;
-constexpr int NS = 4;                  // ring slots (NS-1 stages in flight)
-constexpr int SLOT_BYTES = 32768;      // one K group: weights 16 KB + activations 16 KB
-constexpr int SLOT_X = 0;              // activation rows
-constexpr int SLOT_W = 16384;          // weight columns
 constexpr int SC = 4;                  // groups per scale chunk
-constexpr int SB_BYTES = 4096;         // one scale chunk of E8M0 codes (1024 x u32)
-constexpr int SA_BYTES = 2048;         // one scale chunk of activation scales (512 x fp32)
-constexpr int LDS_SB = NS * SLOT_BYTES;          // 2 buffers
-constexpr int LDS_SA = LDS_SB + 2 * SB_BYTES;    // 2 buffers
-constexpr int LDS_P2_BYTES = LDS_SA + 2 * SA_BYTES;
 
-#define W4A8_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
-#define W4A8_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Each active lane copies 16 (or 4) bytes from its own global address to
-// lds_wave_base + 16 * lane (or 4 * lane).  lds_wave_base must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(W4A8_GPTR(g), W4A8_LPTR(lds_wave_base), 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(W4A8_GPTR(g), W4A8_LPTR(lds_wave_base), 4, 0, 0);
+// ---------------------------------------------------------------------------
+// Vector-memory operations of the K loops are written as inline asm, and every
+// wait for them is explicit.  The compiler cannot tell one LDS ring slot from
+// another, so for a direct-to-LDS load it knows about it would wait for the
+// load to land before any later LDS read, i.e. drain the pipeline every stage;
+// and a mix of loads it sees and loads it does not would make its own register
+// waits force the unseen ones too.  Hence: no compiler-visible vector-memory
+// op inside a K loop, one explicit vmcnt wait per stage (counted from the
+// issue order, which is the completion order of loads), and register loads
+// tied to that wait so that no instruction reads them earlier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// Scalar operands of the asm below must be wave-uniform values the compiler
+// keeps in SGPRs; readfirstlane makes that explicit (and is free when the
+// value already is scalar).  A vector-memory instruction that reads an SGPR
+// written by a VALU instruction (readfirstlane is one) needs 5 wait states in
+// between, and M0 written by SALU needs 1 before a direct-to-LDS load; the
+// compiler inserts such waits for instructions it sees, not inside asm, so
+// each asm below carries its own.
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes per lane from sbase + voff (sbase wave-uniform) to LDS at
+// lds + 16 * lane (lds wave-uniform; lanes outside exec write nothing).
+__device__ __forceinline__ void vm_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane address to LDS at lds + 4 * lane.
+__device__ __forceinline__ void vm_dma4(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(addr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+// 16 bytes per lane into registers; the value may be read only after a wait
+// that covers this load, followed by tie() on the register.
+__device__ __forceinline__ v4i vm_load16(const void* sbase, uint32_t voff) {
+  v4i r;
+  asm volatile("s_nop 4\n\tglobal_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)));
+  return r;
+}
+__device__ __forceinline__ v4i vm_load16_nt(const void* sbase, uint32_t voff) {
+  v4i r;
+  asm volatile("s_nop 4\n\tglobal_load_dwordx4 %0, %1, %2 nt" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)));
+  return r;
+}
+__device__ __forceinline__ void tie(v4i& r) { asm volatile("" : "+v"(r)); }
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory ops in flight.
+// Also a compiler barrier, so no LDS read moves above it.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Wait until at most `pending` later stages of PER_STAGE ring loads each are
-// still in flight, then meet the other waves.  Scale-chunk loads issued with a
-// later stage only make this wait stricter than needed, never looser.
-template <int PER_STAGE>
-__device__ __forceinline__ void stage_barrier(int pending) {
-  static_assert((NS - 2) * PER_STAGE < 64, "too many loads in flight");
-  if (pending >= 2) wait_vm<2 * PER_STAGE>();
-  else if (pending == 1) wait_vm<PER_STAGE>();
-  else wait_vm<0>();
-  __builtin_amdgcn_s_barrier();
+// vmcnt wait for "at most n in flight", n rounded down to a multiple of STEP
+// below N (a stricter wait is always safe).
+template <int N, int STEP>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if constexpr (N <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N>();
+    else wait_vm_at_most<N - STEP, STEP>(n);
+  }
 }
+
+// Workgroup barrier that is also a compiler barrier for memory operations
+// (no fence: the explicit waits decide what has landed).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -133,6 +171,15 @@ __device__ __forceinline__ const float* sa_ptr(const GemmArgs& p, size_t row, in
   return p.layout == 0 ? p.SA + row * (size_t)G + g : p.SA + (size_t)g * R + row;
 }
 
+// A lane index the compiler cannot see through, so that address arithmetic
+// done once per scale chunk is not hoisted out of the K loop (where its
+// registers would compete with the accumulators).
+__device__ __forceinline__ int opaque_lane() {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1: weight streaming (experts with <= S_MAX rows)
 //
@@ -145,8 +192,11 @@ __device__ __forceinline__ const float* sa_ptr(const GemmArgs& p, size_t row, in
 //   X ring   : D+1 slots x [KG][2 halves][64 rows][128 B] @ 0  (row chunk c at c ^ (row & 7))
 //   SB chunk : 2 x [2 halves][64*NBW cols][SC] u32            @ P1_SB
 //   SA chunk : 2 x [2 halves][64 rows][SC] fp32               @ P1_SA
-// After the K loop the halves are added through LDS (always half 0 + half 1,
-// whatever the item width or stage size), then rounded to bf16 and stored.
+// Stage s: wait (the weights of stage s and, older, its activation rows have
+// landed), barrier, issue the activation rows of stage s + D, MFMAs, then the
+// weights of stage s + D into the register slot just used.  After the K loop
+// the halves are added through LDS (always half 0 + half 1, whatever the item
+// width or stage size), then rounded to bf16 and stored.
 // ---------------------------------------------------------------------------
 constexpr int P1_XGROUP = 16384;          // activation rows of one group, both halves
 constexpr int P1_XRING = 6 * P1_XGROUP;   // (D+1)*KG groups, at most 96 KB
@@ -162,36 +212,36 @@ constexpr int P1_SABUF = 2 * 64 * SC * 4;                  // 2 KB
 constexpr int P1_BYTES = P1_SA + 2 * P1_SABUF;
 static_assert(P1_MAXNBW * 16384 <= P1_SB, "reduction scratch must fit below the scale chunks");
 
-template <int NBW, int KG>
+template <int NBW, int KG, int MB>
 struct StreamItem {
   static constexpr int WIDTH = 64 * NBW;  // columns per item
   // stages in flight: KG*D groups of weights per wave
   static constexpr int D = KG == 2 ? 2 : (NBW <= 2 ? 4 : 3);
   static constexpr int NX = D + 1;        // activation ring slots
   static constexpr int XSLOT = KG * P1_XGROUP;
+  static constexpr int PER = KG * (NBW + MB);  // ring loads per wave per stage
   static_assert(NX * XSLOT <= P1_XRING, "activation ring");
+  static_assert((D - 1) * PER < 64, "vmcnt range");
   // a scale chunk buffer is reloaded D stages before the first stage of the
   // chunk after next: every stage of the chunk before must be done by then
   static_assert(SC % KG == 0 && D * KG <= SC, "scale chunk reuse distance");
 
-  // Activation rows of stage s: KG*8*mb loads of 4 rows x 128 B, KG*mb per wave.
-  __device__ __forceinline__ static void issue_x(const GemmArgs& p, uint8_t* slot, int row0, int rows,
-                                                 int mb, int s) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int K = p.K, G = K >> 7, Gh = (G + 1) / 2;
+  // Activation rows of stage s: 8*MB loads of 4 rows x 128 B per group, MB per
+  // wave (half a wave each).  xt = the item's first row.
+  __device__ __forceinline__ static void issue_x(const uint8_t* xt, const uint32_t (&xo)[MB], uint8_t* slot,
+                                                 int G, int s) {
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+    const int Gh = (G + 1) / 2;
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const int g0 = min(s * KG + kg, G - 1), g1 = min(Gh + s * KG + kg, G - 1);
-      for (int i = 0; i < mb; ++i) {
-        if (lane < 32) {
-          const int jx = wave * mb + i;
-          const int h = jx / (4 * mb), quad = jx - h * (4 * mb);
-          const int r = quad * 4 + (lane >> 3);
-          const int c = (lane & 7) ^ (r & 7);
-          const size_t row = (size_t)row0 + min(r, rows - 1);
-          dma16(p.A + row * (size_t)K + (size_t)(h ? g1 : g0) * 128 + c * 16,
-                slot + kg * P1_XGROUP + h * 8192 + quad * 512);
-        }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int jx = wave * MB + i;
+        const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
+        if (lane < 32)
+          vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
+                   lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512));
       }
     }
   }
@@ -199,7 +249,7 @@ struct StreamItem {
   // Scale chunk c (groups SC*c .. SC*c+3 of each half): NBW SB + 1 SA loads per wave.
   __device__ __forceinline__ static void issue_scales(const GemmArgs& p, uint8_t* lds, int e,
                                                       int row0, int rows, int n0, int c, int R) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
     const int K = p.K, N = p.N, G = K >> 7;
     const int gb1 = (G + 1) / 2;
 #pragma unroll
@@ -209,55 +259,49 @@ struct StreamItem {
       const int col = rem >> 2, gg = rem & 3;
       const int n = min(n0 + col, N - 1);
       const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
-      dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-           lds + P1_SB + (c & 1) * P1_SBBUF + (wave * NBW + i) * 256);
+      vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+              lds_u32(lds + P1_SB + (c & 1) * P1_SBBUF + (wave * NBW + i) * 256));
     }
     {
       const int idx = wave * 64 + lane;  // [h][row][gg]
       const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
       const size_t row = (size_t)row0 + min(r, rows - 1);
       const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
-      dma4(sa_ptr(p, row, g, G, R), lds + P1_SA + (c & 1) * P1_SABUF + wave * 256);
+      vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P1_SA + (c & 1) * P1_SABUF + wave * 256));
     }
   }
 
-  // Weight fragments of this wave for stage s (16 B per lane per 16-column block and group).
-  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* const (&wp)[NBW],
-                                                int gfirst, int G) {
+  // Weight fragments of this wave for the stage starting at group gfirst
+  // (16 B per lane per 16-column block and group).  wt = the item's first column.
+  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt,
+                                                const uint32_t (&wo)[NBW], int gfirst, int G) {
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const uint8_t* wg = wt + (size_t)min(gfirst + kg, G - 1) * 64;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) w[kg][j] = vm_load16_nt(wg, wo[j]);
+    }
+  }
+
+  // Wait until the weights of the stage about to be used have landed (at most
+  // `pending` later stages of PER loads each in flight; the stage's activation
+  // rows were issued before its weights), make the weights readable, then meet
+  // the other waves.
+  __device__ __forceinline__ static void stage_wait(int pending, v4i (&w)[KG][NBW]) {
+    if (pending <= 0) wait_vm<0>();
+    else if (pending == 1 || D == 2) wait_vm<PER>();
+    else if (pending == 2 || D == 3) wait_vm<2 * PER>();
+    else wait_vm<(D - 1) * PER>();
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
-        w[kg][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4i*>(wp[j] + (size_t)min(gfirst + kg, G - 1) * 64));
-  }
-
-  // Wait until the activation loads of the stage about to be used have landed
-  // (at most `pending` later stages of KG*(mb + NBW) loads each in flight),
-  // then meet the other waves.
-  template <int PER>
-  __device__ __forceinline__ static void stage_wait(int pending) {
-    static_assert((D - 1) * PER < 64, "too many loads in flight");
-    switch (pending) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<PER>(); break;
-      case 2: wait_vm<(D >= 3 ? 2 : 1) * PER>(); break;
-      default: wait_vm<(D - 1) * PER>(); break;
-    }
-  }
-  __device__ __forceinline__ static void x_barrier(int pending, int mb) {
-    switch (mb) {
-      case 1: stage_wait<KG * (NBW + 1)>(pending); break;
-      case 2: stage_wait<KG * (NBW + 2)>(pending); break;
-      case 3: stage_wait<KG * (NBW + 3)>(pending); break;
-      default: stage_wait<KG * (NBW + 4)>(pending); break;
-    }
-    __builtin_amdgcn_s_barrier();
+      for (int j = 0; j < NBW; ++j) tie(w[kg][j]);
+    wg_barrier();
   }
 
   __device__ __forceinline__ static void run(const GemmArgs& p, uint8_t* lds, int e, int row0,
                                              int rows, int n0, int R) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = opaque_lane(), wave = threadIdx.x >> 6;
     const int kh = wave >> 2, wn = wave & 3;
     const int q = lane >> 4, r16 = lane & 15;
     const int K = p.K, N = p.N, G = K >> 7;
@@ -265,29 +309,38 @@ struct StreamItem {
     const int gbase = kh ? Gh : 0;
     const int gcount = kh == 0 ? Gh : G - Gh;  // groups of this wave's half
     const int S = (Gh + KG - 1) / KG;
-    const int mb = (rows + 15) >> 4;             // 1..4 row blocks
 
-    const uint8_t* wp[NBW];
+    const uint8_t* xt = p.A + (size_t)row0 * K;
+    uint32_t xo[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int jx = uniform(wave) * MB + i;
+      const int quad = jx % (4 * MB);
+      const int r = quad * 4 + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
+    }
+    const uint8_t* wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
+    uint32_t wo[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int n = min(n0 + (wn * NBW + j) * 16 + r16, N - 1);
-      wp[j] = p.B + ((size_t)e * N + n) * (size_t)(K >> 1) + q * 16;
+      wo[j] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
     }
 
-    v4f acc[NBW][4];
+    v4f acc[NBW][MB];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
     v4i wr[D][KG][NBW];
 
-    wait_vm<0>();  // earlier stores must not be counted against this item's loads
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       if (s < S) {
         if ((s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s * KG / SC, R);
-        issue_x(p, lds + (s % NX) * XSLOT, row0, rows, mb, s);
-        load_w(wr[s], wp, gbase + s * KG, G);
+        issue_x(xt, xo, lds + (s % NX) * XSLOT, G, s);
+        load_w(wr[s], wt, wo, gbase + s * KG, G);
       }
     }
 
@@ -296,11 +349,11 @@ struct StreamItem {
       for (int u = 0; u < D; ++u) {
         const int s = s0 + u;
         if (s < S) {
-          x_barrier(min(D - 1, S - 1 - s), mb);
+          stage_wait(min(D - 1, S - 1 - s), wr[u]);
           const int sn = s + D;
           if (sn < S) {
             if ((sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
-            issue_x(p, lds + (sn % NX) * XSLOT, row0, rows, mb, sn);
+            issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, sn);
           }
           const uint8_t* slot = lds + (s % NX) * XSLOT;
 #pragma unroll
@@ -317,42 +370,39 @@ struct StreamItem {
                 sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
               }
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if (i < mb) {
-                  const int m = i * 16 + r16;
-                  const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
-                  const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
-                  const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
-                  const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
+              for (int i = 0; i < MB; ++i) {
+                const int m = i * 16 + r16;
+                const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
+                const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
+                const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
+                const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
 #pragma unroll
-                  for (int j = 0; j < NBW; ++j)
-                    promote(acc[j][i], sa, mfma_group(wr[u][kg][j], x0, x1, sbv[j]));
-                }
+                for (int j = 0; j < NBW; ++j)
+                  promote(acc[j][i], sa, mfma_group(wr[u][kg][j], x0, x1, sbv[j]));
               }
             }
           }
-          if (sn < S) load_w(wr[u], wp, gbase + sn * KG, G);
+          if (sn < S) load_w(wr[u], wt, wo, gbase + sn * KG, G);
         }
       }
     }
 
-    // add the two K halves in LDS (nothing is in flight and every wave is past
-    // its last LDS read after this barrier) and store
+    // add the two K halves in LDS (nothing is in flight -- the last wait was
+    // for zero -- and every wave is past its last LDS read after this barrier)
     __syncthreads();
     v4f* red = reinterpret_cast<v4f*>(lds);
     if (kh == 1) {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i < mb) red[((wn * NBW + j) * 4 + i) * 64 + lane] = acc[j][i];
+        for (int i = 0; i < MB; ++i) red[((wn * NBW + j) * 4 + i) * 64 + lane] = acc[j][i];
     }
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MB; ++i) {
         const int m = i * 16 + r16;
-        if (i < mb && m < rows) {
+        if (m < rows) {
           uint16_t* crow = p.C + (size_t)(row0 + m) * N;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
@@ -366,6 +416,17 @@ struct StreamItem {
     __syncthreads();  // red is overwritten by the next item's loads
   }
 };
+
+template <int NBW>
+__device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
+                                            int n0, int R) {
+  switch ((rows + 15) >> 4) {
+    case 1: StreamItem<NBW, P1_KG, 1>::run(p, lds, e, row0, rows, n0, R); break;
+    case 2: StreamItem<NBW, P1_KG, 2>::run(p, lds, e, row0, rows, n0, R); break;
+    case 3: StreamItem<NBW, P1_KG, 3>::run(p, lds, e, row0, rows, n0, R); break;
+    default: StreamItem<NBW, P1_KG, 4>::run(p, lds, e, row0, rows, n0, R); break;
+  }
+}
 
 // Item width for the streaming phase: the width (64*NBW columns) that
 // minimises rounds x per-item bytes, per-item bytes ~ weights (32*NBW per K)
@@ -387,137 +448,313 @@ __device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: MFMA tiles (larger experts), 256(n) x 128(m), one group per stage.
-// Ring slot:  X [128 rows][128 B] @ SLOT_X   (row chunk c at c ^ (row & 7))
-//             W [256 cols][64 B]  @ SLOT_W   (col chunk c at c ^ ((col >> 1) & 3))
-// Scale chunk c (groups SC*c .. SC*c+3):  SB [256 cols][SC] u32;  SA [128 rows][SC] fp32
+// Phase 2: MFMA tiles (larger experts), 512(n) x 128(m) per workgroup.
+//
+// Wave w owns columns 64w .. 64w+63 of the tile and all of its rows (4 x 8
+// MFMA blocks, 128 fp32 accumulators per lane).  Every weight byte of the
+// tile is needed by exactly one wave, so weights go from global memory
+// straight into that wave's MFMA operand registers (the next group's weights
+// load while the current group's are in use); only the activation rows and
+// the scales, which every wave needs, are staged in LDS:
+//   X ring   : P2_NX slots x [128 rows][128 B]  (row chunk c at c ^ (row & 7))
+//   SB chunk : 2 x [512 cols][SC] u32  (E8M0 codes of groups SC*c .. SC*c+3)
+//   SA chunk : 2 x [128 rows][SC] fp32
+// Stage s (one K group): wait (weights of group s and, older, its activation
+// rows have landed), barrier, issue the weights of group s + 1 and then the
+// activation rows of group s + 2 (with their scale chunk), then 32 MFMAs per
+// wave.  One in-order counter per wave is what sets the depths: waiting for
+// the weights of group s also waits for everything issued before them, so
+// activation rows are issued right after a weight load and run one stage
+// further ahead than the weights.
+// Per 128-K group a workgroup reads 32 KB of weights and 16 KB of activations
+// for 256 MFMAs, the fewest bytes per MFMA of the tile shapes whose
+// accumulators fit two waves per SIMD.
 // ---------------------------------------------------------------------------
-constexpr int MF_BN = TN_MFMA;  // 256 weight columns
-constexpr int MF_BM = T_MAX;    // 128 activation rows
-constexpr int P2_PER_STAGE = 4; // W 2, X 2 ring loads per wave
+constexpr int MF_BN = TN_MFMA;          // 512 weight columns
+constexpr int MF_BM = T_MAX;            // 128 activation rows
+constexpr int P2_DW = 1;                // weight groups ahead (register slots: P2_DW + 1)
+constexpr int P2_DX = P2_DW + 1;        // activation groups ahead
+constexpr int P2_NX = P2_DX + 1;        // activation ring slots
+constexpr int P2_XSLOT = MF_BM * 128;   // 16 KB
+constexpr int P2_SB = P2_NX * P2_XSLOT;
+constexpr int P2_SBBUF = MF_BN * SC * 4;  // 8 KB
+constexpr int P2_SA = P2_SB + 2 * P2_SBBUF;
+constexpr int P2_SABUF = MF_BM * SC * 4;  // 2 KB
+constexpr int P2_BYTES = P2_SA + 2 * P2_SABUF;
+constexpr int P2_X_OPS = 2;             // activation loads per wave per stage
+constexpr int P2_W_OPS = 4;             // weight loads per wave per stage
+constexpr int P2_WAIT_MAX = P2_X_OPS + (P2_DW - 1) * (P2_X_OPS + P2_W_OPS);
+// a scale buffer is refilled P2_DX stages ahead, after every stage of the
+// chunk two back has passed the barrier of the stage that refills it
+static_assert(P2_DX <= SC, "scale chunk reuse distance");
+static_assert(P2_DW == 1, "the stage loop is unrolled for two weight slots");
 
-__device__ __forceinline__ void mf_issue_stage(const GemmArgs& p, uint8_t* slot, int e, int row0,
-                                               int rows, int n0, int g) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = p.K, N = p.N;
+// Vector-memory ops this wave issues after the weights of stage s (scale
+// chunks not counted, which only makes the wait stricter).  Iteration t
+// issues W(t + P2_DW) and then X(t + P2_DX); the prologue is iterations
+// -P2_DX .. -1 under the same rule.
+__device__ __forceinline__ int p2_ops_after_w(int s, int G) {
+  const int t0 = s - P2_DW;
+  int n = (t0 + P2_DX < G) ? P2_X_OPS : 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int j = wave * 2 + i;  // 16 columns x 64 B
-    const int r = j * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 1) & 3);
-    const int n = min(n0 + r, N - 1);
-    dma16(p.B + ((size_t)e * N + n) * (size_t)(K >> 1) + (size_t)g * 64 + c * 16, slot + SLOT_W + j * 1024);
+  for (int d = 1; d < P2_DW; ++d) {
+    const int t = t0 + d;
+    if (t + P2_DW < G) n += P2_W_OPS;
+    if (t + P2_DX < G) n += P2_X_OPS;
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int j = wave * 2 + i;  // 8 rows x 128 B
-    const int r = j * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    const size_t row = (size_t)row0 + min(r, rows - 1);
-    dma16(p.A + row * (size_t)K + (size_t)g * 128 + c * 16, slot + SLOT_X + j * 1024);
-  }
+  return n;
 }
 
-__device__ __forceinline__ void mf_issue_scales(const GemmArgs& p, uint8_t* lds, int e, int row0,
+// Activation rows of group g: 128 rows x 128 B, two 8-row loads per wave
+// (xt = the tile's first row, xo = this lane's byte offsets from it).
+__device__ __forceinline__ void p2_issue_x(const uint8_t* xt, const uint32_t (&xo)[P2_X_OPS],
+                                           uint8_t* slot, int g) {
+  const int wave = uniform(threadIdx.x >> 6);
+  const uint8_t* xg = xt + (size_t)g * 128;
+#pragma unroll
+  for (int i = 0; i < P2_X_OPS; ++i) vm_dma16(xg, xo[i], lds_u32(slot + (wave * P2_X_OPS + i) * 1024));
+}
+
+// Scale chunk c: 512 columns x SC groups of E8M0 words (four loads per wave)
+// and 128 rows x SC groups of activation scales (one load per wave).
+__device__ __forceinline__ void p2_issue_scales(const GemmArgs& p, uint8_t* lds, int e, int row0,
                                                 int rows, int n0, int c, int R) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
   const int K = p.K, N = p.N, G = K >> 7;
+  const int gg = lane & 3;
+  const int g = min(SC * c + gg, G - 1);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = (wave * 2 + i) * 64 + lane;  // [col][gg]
-    const int col = idx >> 2, gg = idx & 3;
+  for (int i = 0; i < 4; ++i) {
+    const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // [col][gg]
     const int n = min(n0 + col, N - 1);
-    const int g = min(SC * c + gg, G - 1);
-    dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-         lds + LDS_SB + (c & 1) * SB_BYTES + (wave * 2 + i) * 256);
+    vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+            lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
   }
-  {
-    const int idx = wave * 64 + lane;  // [row][gg]
-    const int r = idx >> 2, gg = idx & 3;
-    const size_t row = (size_t)row0 + min(r, rows - 1);
-    const int g = min(SC * c + gg, G - 1);
-    dma4(sa_ptr(p, row, g, G, R), lds + LDS_SA + (c & 1) * SA_BYTES + wave * 256);
+  const int r = (wave * 64 + lane) >> 2;  // [row][gg]
+  const size_t row = (size_t)row0 + min(r, rows - 1);
+  vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P2_SA + (c & 1) * P2_SABUF + wave * 256));
+}
+
+// Weights of group g for this wave's four 16-column blocks (wt = the tile's
+// first column, wo = this lane's byte offsets from it).
+__device__ __forceinline__ void p2_load_w(v4i (&w)[4], const uint8_t* wt, const uint32_t (&wo)[4], int g) {
+  const uint8_t* wg = wt + (size_t)g * 64;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) w[nb] = vm_load16(wg, wo[nb]);
+}
+
+// LDS addresses of this lane's fragments in a stage slot / scale buffer: row
+// block mi adds the immediate mi * 2048 (X) or mi * 256 (SA).  Row m = 16 mi
+// + i has swizzle key m & 7 = i & 7 for every mi.
+struct P2Lds {
+  const uint8_t* x0;  // chunk q of row i
+  const uint8_t* x1;  // chunk q + 4 of row i
+  const uint8_t* sa;  // scale (row i, group gg)
+};
+
+__device__ __forceinline__ void p2_read_x(const P2Lds& a, int mi, v4i& x0, v4i& x1, float& sa) {
+  x0 = lds128(a.x0 + mi * 2048);
+  x1 = lds128(a.x1 + mi * 2048);
+  sa = ldsf(a.sa + mi * 16 * SC * 4);
+}
+
+// One K group for NMB row blocks.  Step mi issues the LDS reads of block
+// mi+1, the promotion of the previous step's partials (carried across stages
+// in prev/sprev, so the first step of a stage has arithmetic to do while its
+// reads are in flight) and the four MFMAs of block mi; the scheduling fences
+// keep each step's work together.
+template <int NMB>
+__device__ __forceinline__ void p2_group(v4f (&acc)[8][4], v4f (&prev)[4], float& sprev, const v4i (&w)[4],
+                                         const P2Lds& a, const int (&sbv)[4]) {
+  v4i xa0, xa1;
+  float saa;
+  p2_read_x(a, 0, xa0, xa1, saa);
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    v4i xb0 = xa0, xb1 = xa1;
+    float sab_n = saa;
+    if (mi + 1 < NMB) p2_read_x(a, mi + 1, xb0, xb1, sab_n);
+    // the previous step's block: the last block of the previous group when mi == 0
+    const int pm = mi == 0 ? NMB - 1 : mi - 1;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) promote(acc[pm][nb], sprev, prev[nb]);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) prev[nb] = mfma_group(w[nb], xa0, xa1, sbv[nb]);
+    sprev = saa;
+    xa0 = xb0;
+    xa1 = xb1;
+    saa = sab_n;
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
+
+template <int NMB>
+struct MfmaTile {
+  const GemmArgs& p;
+  uint8_t* lds;
+  int e, row0, rows, n0, R, G, wn, q, r16, xl0, xl1;
+  bool wvalid;
+  const uint8_t* xt;
+  const uint8_t* wt;
+  uint32_t xo[P2_X_OPS];
+  uint32_t wo[4];
+
+  __device__ __forceinline__ MfmaTile(const GemmArgs& p_, uint8_t* lds_, int e_, int row0_, int rows_,
+                                      int n0_, int R_)
+      : p(p_), lds(lds_), e(e_), row0(row0_), rows(rows_), n0(n0_), R(R_) {
+    // opaque lane: the per-lane constants below are computed per tile, not
+    // hoisted out of the tile loop where they would be live across it
+    const int lane = opaque_lane(), wave = threadIdx.x >> 6;
+    const int K = p.K, N = p.N;
+    G = K >> 7;
+    wn = wave;
+    q = lane >> 4;
+    r16 = lane & 15;
+    wvalid = uniform(n0 + wn * 64) < N;  // wave has columns inside N
+    // tile bases (uniform) and per-lane 32-bit offsets: K <= 2^20 keeps every
+    // in-tile offset below 2^32
+    xt = p.A + (size_t)row0 * K;
+    wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
+#pragma unroll
+    for (int i = 0; i < P2_X_OPS; ++i) {
+      const int r = (wave * P2_X_OPS + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = min(n0 + wn * 64 + nb * 16 + r16, N - 1);
+      wo[nb] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
+    }
+    // LDS byte offsets of this lane's activation fragments within a slot
+    xl0 = r16 * 128 + ((q ^ (r16 & 7)) << 4);
+    xl1 = r16 * 128 + (((q + 4) ^ (r16 & 7)) << 4);
+  }
+
+  // loads of iteration t of the issue rule: W(t + P2_DW) into wnext, X(t + P2_DX)
+  __device__ __forceinline__ void issue(int t, v4i (&wnext)[4]) {
+    const int sw = t + P2_DW;
+    if (sw >= 0 && sw < G) p2_load_w(wnext, wt, wo, sw);
+    const int sx = t + P2_DX;
+    if (sx < G) {
+      if (sx % SC == 0) p2_issue_scales(p, lds, e, row0, rows, n0, sx / SC, R);
+      p2_issue_x(xt, xo, lds + (sx % P2_NX) * P2_XSLOT, sx);
+    }
+  }
+
+  __device__ __forceinline__ void stage(int s, v4i (&wcur)[4], v4i (&wnext)[4], v4f (&acc)[8][4],
+                                        v4f (&prev)[4], float& sprev) {
+    wait_vm_at_most<P2_WAIT_MAX, 2>(p2_ops_after_w(s, G));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) tie(wcur[nb]);
+    wg_barrier();
+    issue(s, wnext);
+    if (wvalid) {
+      const uint8_t* slot = lds + (s % P2_NX) * P2_XSLOT;
+      const uint8_t* sbb = lds + P2_SB + ((s / SC) & 1) * P2_SBBUF;
+      const uint8_t* sab = lds + P2_SA + ((s / SC) & 1) * P2_SABUF;
+      const int gg = s % SC;
+      int sbv[4];
+      const uint8_t* sbl = sbb + ((wn * 64 + r16) * SC + gg) * 4;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) sbv[nb] = (int)((lds32(sbl + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
+      P2Lds a;
+      a.x0 = slot + xl0;
+      a.x1 = slot + xl1;
+      a.sa = sab + (r16 * SC + gg) * 4;
+      p2_group<NMB>(acc, prev, sprev, wcur, a, sbv);
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    // zero accumulators, made opaque so that the compiler does not peel the
+    // first K group to specialise it for zero inputs (a second copy of the
+    // loop body with its own register assignment)
+    v4f acc[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+v"(acc[a][b]));
+      }
+    v4f prev[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      prev[b] = v4f{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+v"(prev[b]));
+    }
+    float sprev = 0.f;
+    asm volatile("" : "+v"(sprev));
+    v4i w0[4], w1[4];
+
+    // prologue = iterations -P2_DX .. -1 of the issue rule; W(0) lands in w0
+    issue(-2, w1);
+    issue(-1, w0);
+    for (int s = 0; s < G; s += 2) {
+      stage(s, w0, w1, acc, prev, sprev);
+      if (s + 1 < G) stage(s + 1, w1, w0, acc, prev, sprev);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) promote(acc[NMB - 1][nb], sprev, prev[nb]);
+    __syncthreads();  // every wave is done with the ring before the next tile's loads
+
+    if (wvalid) {
+      // lane coordinates recomputed (opaque) rather than kept live through the K loop
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+      const int eq = (t >> 4) & 3, er = t & 15;
+      const int ncol = n0 + (t >> 6) * 64 + eq * 4;
+      const int N = p.N;
+#pragma unroll
+      for (int mi = 0; mi < NMB; ++mi) {
+        const int m = mi * 16 + er;
+        if (m < rows) {
+          uint16_t* crow = p.C + (size_t)(row0 + m) * N;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int n = ncol + nb * 16;
+            if (n < N) store_bf16x4(crow + n, acc[mi][nb]);
+          }
+        }
+      }
+    }
+  }
+};
+static_assert(P2_DX == 2, "the prologue issues iterations -2 and -1");
 
 __device__ __forceinline__ void mfma_tile(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
                                           int n0, int R) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave & 3, wm = wave >> 2;  // 4 waves along n (64 each), 2 along m
-  const int q = lane >> 4, r16 = lane & 15;
-  const int G = p.K >> 7;
-  // row blocks of this wave that hold real rows: wm, wm+2, wm+4, wm+6
-  const int nmb = uniform(rows > wm * 16 ? min(4, (rows - wm * 16 + 31) / 32) : 0);
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  wait_vm<0>();
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) {
-    if (s < G) {
-      if (s % SC == 0) mf_issue_scales(p, lds, e, row0, rows, n0, s / SC, R);
-      mf_issue_stage(p, lds + s * SLOT_BYTES, e, row0, rows, n0, s);
-    }
+  switch ((rows + 15) >> 4) {
+    case 1: MfmaTile<1>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 2: MfmaTile<2>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 3: MfmaTile<3>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 4: MfmaTile<4>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 5: MfmaTile<5>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 6: MfmaTile<6>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 7: MfmaTile<7>(p, lds, e, row0, rows, n0, R).run(); break;
+    default: MfmaTile<8>(p, lds, e, row0, rows, n0, R).run(); break;
   }
+}
 
-  for (int g = 0; g < G; ++g) {
-    stage_barrier<P2_PER_STAGE>(min(NS - 2, G - 1 - g));
-    const int gn = g + NS - 1;
-    if (gn < G) {
-      if (gn % SC == 0) mf_issue_scales(p, lds, e, row0, rows, n0, gn / SC, R);
-      mf_issue_stage(p, lds + (gn % NS) * SLOT_BYTES, e, row0, rows, n0, gn);
-    }
-    const uint8_t* slot = lds + (g % NS) * SLOT_BYTES;
-    const uint8_t* sbb = lds + LDS_SB + ((g / SC) & 1) * SB_BYTES;
-    const uint8_t* sab = lds + LDS_SA + ((g / SC) & 1) * SA_BYTES;
-    const int gg = g % SC;
-    v4i wf[4];
-    int sbv[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = wn * 64 + nb * 16 + r16;
-      wf[nb] = lds128(slot + SLOT_W + n * 64 + ((q ^ ((n >> 1) & 3)) << 4));
-      sbv[nb] = (int)((lds32(sbb + (n * SC + gg) * 4) >> (8 * q)) & 0xffu);
-    }
-    v4i x0[4], x1[4];
-    float sa[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int m = (wm + 2 * mi) * 16 + r16;
-      const uint8_t* xb = slot + SLOT_X + m * 128;
-      x0[mi] = lds128(xb + ((q ^ (m & 7)) << 4));
-      x1[mi] = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
-      sa[mi] = ldsf(sab + (m * SC + gg) * 4);
-    }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      if (mi < nmb) {
-        v4f pr[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) pr[nb] = mfma_group(wf[nb], x0[mi], x1[mi], sbv[nb]);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) promote(acc[mi][nb], sa[mi], pr[nb]);
-      }
-    }
-  }
-  __syncthreads();  // every wave is done with the ring before the next tile's loads
+// Work item of round r for workgroup b.  Workgroups are dealt to the eight
+// XCDs round-robin (b % 8), each XCD with its own L2, so the items of one
+// round are regrouped to give every XCD a contiguous block of item numbers.
+__device__ __forceinline__ int xcd_item(int r, int b, int grid) {
+  if ((grid & 7) != 0) return r * grid + b;
+  return r * grid + (b & 7) * (grid >> 3) + (b >> 3);
+}
 
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int m = (wm + 2 * mi) * 16 + r16;
-    if (m < rows) {
-      uint16_t* crow = p.C + (size_t)(row0 + m) * p.N;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + wn * 64 + nb * 16 + q * 4;
-        if (n < p.N) store_bf16x4(crow + n, acc[mi][nb]);
-      }
-    }
-  }
+// Item number -> (m-tile, n-tile): bands of P2_SUPER m-tiles, n-tiles in
+// order within a band and m fastest, so a block of consecutive items shares
+// a few m-tiles (activation rows) and a few n-tiles (weight columns).
+constexpr int P2_SUPER = 4;
+__device__ __forceinline__ void item_tile(int L, int MT, int NT, int* mt, int* nt) {
+  const int band = L / (P2_SUPER * NT);
+  const int rem = L - band * P2_SUPER * NT;
+  const int rg = min(P2_SUPER, MT - band * P2_SUPER);
+  *mt = band * P2_SUPER + rem % rg;
+  *nt = rem / rg;
 }
 
 // ---------------------------------------------------------------------------
@@ -525,7 +762,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& p, uint8_t* lds, int e
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(BLOCK, 1)
 grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_P2_BYTES > P1_BYTES ? LDS_P2_BYTES : P1_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[P2_BYTES > P1_BYTES ? P2_BYTES : P1_BYTES];
   __shared__ int s_off[MAX_EXPERTS + 1];
   __shared__ int s_sbase[MAX_EXPERTS + 1];
   __shared__ int s_mbase[MAX_EXPERTS + 1];
@@ -547,20 +784,26 @@ grouped_gemm_kernel(GemmArgs p) {
       const int row0 = uniform(s_off[e]);
       const int rows = uniform(s_off[e + 1]) - row0;
       switch (nbw) {
-        case 1: StreamItem<1, P1_KG>::run(p, lds, e, row0, rows, n0, R); break;
-        case 2: StreamItem<2, P1_KG>::run(p, lds, e, row0, rows, n0, R); break;
-        default: StreamItem<3, P1_KG>::run(p, lds, e, row0, rows, n0, R); break;
+        case 1: stream_item<1>(p, lds, e, row0, rows, n0, R); break;
+        case 2: stream_item<2>(p, lds, e, row0, rows, n0, R); break;
+        default: stream_item<3>(p, lds, e, row0, rows, n0, R); break;
       }
     }
   }
 
   // phase 2: MFMA tiles, one workgroup each
   {
-    const int nt_count = (p.N + MF_BN - 1) / MF_BN;
-    const long long items = (long long)uniform(s_mbase[p.E]) * nt_count;
-    for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-      const int mt = (int)(it / nt_count);
-      const int n0 = (int)(it % nt_count) * MF_BN;
+    // MT <= R / 65 + E and NT <= 2^31 / 512 keep the item count in 32 bits
+    const int MT = uniform(s_mbase[p.E]);
+    const int NT = (p.N + MF_BN - 1) / MF_BN;
+    const int items = MT * NT;
+    const int grid = gridDim.x;
+    const int rounds = (items + grid - 1) / grid;
+    for (int r = 0; r < rounds; ++r) {
+      const int L = xcd_item(r, blockIdx.x, grid);
+      if (L >= items) continue;
+      int mt, nt;
+      item_tile(L, MT, NT, &mt, &nt);
       const int e = uniform(expert_of_tile(s_mbase, p.E, mt));
       const int j = mt - uniform(s_mbase[e]);
       const int base = uniform(s_off[e]);
@@ -568,7 +811,7 @@ grouped_gemm_kernel(GemmArgs p) {
       const TileChoice tc = tile_rule(rows_e);
       const int row0 = base + j * tc.tile_m;
       const int rows = min(tc.tile_m, rows_e - j * tc.tile_m);
-      mfma_tile(p, lds, e, row0, rows, n0, R);
+      mfma_tile(p, lds, e, row0, rows, nt * MF_BN, R);
     }
   }
 }

@@ -137,7 +137,7 @@ plan_kernel(const int32_t* __restrict__ offsets, int E, int N, int32_t* __restri
     plan[1] = total;
     plan[2] = ns;
     plan[3] = nm;
-    plan[4] = ns * (N / TN_STREAM);
+    plan[4] = ns * ((N + TN_STREAM - 1) / TN_STREAM);
     plan[5] = nm * ((N + TN_MFMA - 1) / TN_MFMA);
     plan[6] = padded;
     plan[7] = s_off[E];

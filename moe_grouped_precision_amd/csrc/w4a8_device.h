@@ -16,14 +16,15 @@ namespace w4a8 {
 // (last note under that page's tables).  Small experts go to a separate
 // small-M schedule below a cutoff (commit 2 "Small-expert seed tile").
 // Constants are this library's own: GRAN is one MFMA block of rows, S_MAX the
-// largest expert the weight-streaming kernel serves (four MFMA blocks), T_MAX
-// the MFMA kernel's largest m-tile.
+// largest expert the weight-streaming phase serves (four MFMA blocks), T_MAX
+// the MFMA phase's m-tile; TN_STREAM is the n granularity of streaming work
+// (a workgroup item holds 1-3 of these), TN_MFMA the MFMA phase's n-tile.
 // ---------------------------------------------------------------------------
 constexpr int GRAN = 16;
 constexpr int S_MAX = 64;
 constexpr int T_MAX = 128;
-constexpr int TN_STREAM = 32;
-constexpr int TN_MFMA = 256;
+constexpr int TN_STREAM = 64;
+constexpr int TN_MFMA = 512;
 constexpr int PLAN_HEADER_WORDS = 8;
 constexpr int PLAN_TILE_WORDS = 4;
 

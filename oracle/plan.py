@@ -24,7 +24,7 @@ Plan layout (int32): an 8-word header, then 4 words per m-tile.
   tile:   [expert, first_row, rows, tile_m | class << 16]
 STREAM tiles come first, then MFMA tiles; each class is in (expert, i)
 order.  A work item is one m-tile times one n-tile of the class's width;
-stream_items = stream_m_tiles * N/TN_STREAM,
+stream_items = stream_m_tiles * ceil(N/TN_STREAM),
 mfma_items   = mfma_m_tiles * ceil(N/TN_MFMA).
 status: 0 ok, 1 offsets invalid (offsets[0] != 0 or decreasing),
         2 the caller's buffer holds fewer tiles than the plan has.
@@ -38,8 +38,8 @@ import numpy as np
 GRAN = 16          # m granularity: rows of one MFMA block
 S_MAX = 64         # largest expert served by the weight-streaming class
 T_MAX = 128        # largest m-tile of the MFMA class
-TN_STREAM = 32     # n width of one streaming work item
-TN_MFMA = 256      # n width of one MFMA work item
+TN_STREAM = 64     # n granularity of streaming work (a workgroup item holds 1-3 of them)
+TN_MFMA = 512      # n width of one MFMA work item
 
 CLASS_NONE, CLASS_STREAM, CLASS_MFMA = 0, 1, 2
 HEADER_WORDS = 8
@@ -86,7 +86,7 @@ def plan_ref(offsets, E: int, N: int, max_tiles=None) -> np.ndarray:
             tiles[cls].append((e, int(off[e]) + r0, r, tile_m | (cls << 16)))
             padded += tile_m - r
     ns, nm = len(tiles[CLASS_STREAM]), len(tiles[CLASS_MFMA])
-    hdr[1:8] = (ns + nm, ns, nm, ns * (N // TN_STREAM), nm * _ceil_div(N, TN_MFMA),
+    hdr[1:8] = (ns + nm, ns, nm, ns * _ceil_div(N, TN_STREAM), nm * _ceil_div(N, TN_MFMA),
                 padded, int(off[E]))
     body = tiles[CLASS_STREAM] + tiles[CLASS_MFMA]
     if max_tiles is not None and len(body) > max_tiles:

@@ -105,8 +105,9 @@ def test_tile_rule_exact_fit():
     for n in range(1, 40):
         cls, tile_m, n_m = tile_rule(n * P.T_MAX)
         assert (tile_m, n_m) == (P.T_MAX, n)
-    # and the uneven case the fixed-M128 rule got wrong: 130 rows -> 2 tiles of 80
-    assert tile_rule(130) == (P.CLASS_MFMA, 80, 2)
+    # an expert just past one full tile gets two balanced tiles, not a full
+    # tile plus a nearly empty one
+    assert tile_rule(P.T_MAX + 2) == (P.CLASS_MFMA, -(-(P.T_MAX // 2 + 1) // P.GRAN) * P.GRAN, 2)
 
 
 def test_plan_layout_and_stats():
@@ -120,7 +121,7 @@ def test_plan_layout_and_stats():
     plan = plan_ref(off, E, N)
     hdr, body = plan[:8], plan[8:].reshape(-1, 4)
     assert hdr[0] == 0 and hdr[1] == len(body) == hdr[2] + hdr[3]
-    assert hdr[4] == hdr[2] * (N // P.TN_STREAM) and hdr[5] == hdr[3] * (N // P.TN_MFMA)
+    assert hdr[4] == hdr[2] * -(-N // P.TN_STREAM) and hdr[5] == hdr[3] * -(-N // P.TN_MFMA)
     assert hdr[7] == off[-1]
     cls = body[:, 3] >> 16
     assert np.all(cls[: hdr[2]] == P.CLASS_STREAM) and np.all(cls[hdr[2]:] == P.CLASS_MFMA)
@@ -142,7 +143,7 @@ def test_plan_bad_offsets_and_capacity():
     assert plan_ref(np.array([0, 5, 3]), 2, 256)[0] == P.STATUS_BAD_OFFSETS
     full = plan_ref(np.array([0, 300, 301]), 2, 256)
     capped = plan_ref(np.array([0, 300, 301]), 2, 256, max_tiles=2)
-    assert capped[0] == P.STATUS_CAPACITY and full[1] == 4
+    assert capped[0] == P.STATUS_CAPACITY and full[1] == -(-300 // P.T_MAX) + 1
     assert np.array_equal(capped[8:], full[8:16])
     empty = plan_ref(np.zeros(9, dtype=np.int32), 8, 256)
     assert list(empty) == [0] * 8
