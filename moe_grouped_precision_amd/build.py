@@ -48,10 +48,38 @@ def compile_flags(debug: bool = False):
     return flags
 
 
+# sources whose K loops issue inline-asm memory operations: their device
+# assembly is checked after every build (see asmcheck.py)
+ASM_CHECKED = ["gemm.hip"]
+
+
+def check_device_asm(cc: str, tmp: str, verbose: bool = False) -> None:
+    """Emit the gfx950 assembly of the inline-asm kernels and run the static
+    check on it; raise if it reports anything."""
+    from . import asmcheck
+
+    for src in ASM_CHECKED:
+        path = os.path.join(CSRC, src)
+        asm = os.path.join(tmp, src.replace(".", "_") + ".s")
+        cmd = [cc, "-x", "hip", *compile_flags(), "--cuda-device-only", "-S", path, "-o", asm]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed on {src}:\n{res.stderr}")
+        findings = asmcheck.check(asm)
+        if findings:
+            raise RuntimeError(f"device assembly of {src} fails the load/wait check:\n" +
+                               "\n".join(findings[:20]))
+
+
 def build(verbose: bool = False, debug: bool = False) -> str:
-    """Compile every source and link libw4a8.so; returns the library path."""
+    """Compile every source, check the device assembly of the inline-asm
+    kernels, and link libw4a8.so; returns the library path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="w4a8_build_") as tmp:
+        if not debug:
+            check_device_asm(cc, tmp, verbose)
         objs = []
         for src in SOURCES:
             path = os.path.join(CSRC, src)

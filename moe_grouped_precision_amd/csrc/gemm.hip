@@ -33,8 +33,8 @@
 //      (always half 0 + half 1) before the bf16 store.
 //   2. MFMA tiles (larger experts): 512(n) x 128(m) per workgroup, one K group
 //      per stage; each wave owns 64 columns x all 128 rows, its weights in a
-//      register ring, the activation rows in a 4-slot LDS ring (three stages
-//      in flight); tiles are dealt so that each XCD works on a compact block.
+//      register ring, the activation rows in an LDS ring; tiles are dealt so
+//      that each XCD works on a compact block.
 // Shared operands reach LDS through direct global->LDS loads
 // (global_load_lds_dwordx4 / _dword), which hold no registers while in
 // flight: every wave issues the same number of loads per stage, waits for the
@@ -71,9 +71,10 @@ constexpr int SC = 4;                  // groups per scale chunk
 // issue order, which is the completion order of loads), and register loads
 // tied to that wait so that no instruction reads them earlier.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
+// LDS byte address of a pointer into the kernel's shared array: the low 32
+// bits of its flat address (the shared aperture is 4 GB aligned).  Taking
+// them directly avoids the null test of a generic-to-local address cast.
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return (uint32_t)(uintptr_t)p; }
 
 // Scalar operands of the asm below must be wave-uniform values the compiler
 // keeps in SGPRs; readfirstlane makes that explicit (and is free when the
@@ -95,6 +96,17 @@ __device__ __forceinline__ void vm_dma16(const void* sbase, uint32_t voff, uint3
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
+// The same for lanes 0-31 only (lds + 16 * lane, 512 bytes): the asm masks the
+// upper half of exec itself, so the load is one straight-line instruction that
+// every wave issues, not a branch around it.
+__device__ __forceinline__ void vm_dma16_lo(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint64_t saved;
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_hi, 0\n\ts_mov_b32 m0, %3\n\ts_nop 3\n\t"
+               "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0", "exec");
+}
 // 4 bytes per lane from a per-lane address to LDS at lds + 4 * lane.
 __device__ __forceinline__ void vm_dma4(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -114,24 +126,13 @@ __device__ __forceinline__ v4i vm_load16_nt(const void* sbase, uint32_t voff) {
 }
 __device__ __forceinline__ void tie(v4i& r) { asm volatile("" : "+v"(r)); }
 
+
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory ops in flight.
 // Also a compiler barrier, so no LDS read moves above it.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// vmcnt wait for "at most n in flight", n rounded down to a multiple of STEP
-// below N (a stricter wait is always safe).
-template <int N, int STEP>
-__device__ __forceinline__ void wait_vm_at_most(int n) {
-  if constexpr (N <= 0) {
-    wait_vm<0>();
-  } else {
-    if (n >= N) wait_vm<N>();
-    else wait_vm_at_most<N - STEP, STEP>(n);
-  }
 }
 
 // Workgroup barrier that is also a compiler barrier for memory operations
@@ -170,6 +171,20 @@ __device__ __forceinline__ float ldsf(const uint8_t* p) { return *reinterpret_ca
 __device__ __forceinline__ const float* sa_ptr(const GemmArgs& p, size_t row, int g, int G, int R) {
   return p.layout == 0 ? p.SA + row * (size_t)G + g : p.SA + (size_t)g * R + row;
 }
+
+// Activation rows are stored 128 B per row in LDS with 16-byte chunk c of
+// row r at position c ^ xkey(r).  A 16-byte read serves 16 lanes per pass
+// over 64 four-byte banks, i.e. two rows' worth of banks: the 16 lanes of a
+// fragment read (rows 16j .. 16j+15, one chunk index) then hit 16 distinct
+// 4-bank groups -- rows of one parity share a bank half and differ in r >> 1.
+__device__ __forceinline__ int xkey(int r) { return (r >> 1) & 7; }
+
+// Scale words are stored in rows of SCW 4-byte words (one row per weight column
+// or activation row), word gg of row r at position gg ^ skey<SCW>(r).  A 4-byte
+// read of 16 consecutive rows is served by 32 banks: without the key, rows r
+// and r + 32/SCW would share a bank; with it they differ in position.
+template <int SCW>
+__device__ __forceinline__ int skey(int r) { return (r / (32 / SCW)) & (SCW - 1); }
 
 // A lane index the compiler cannot see through, so that address arithmetic
 // done once per scale chunk is not hoisted out of the K loop (where its
@@ -239,9 +254,8 @@ struct StreamItem {
       for (int i = 0; i < MB; ++i) {
         const int jx = wave * MB + i;
         const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
-        if (lane < 32)
-          vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
-                   lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512));
+        vm_dma16_lo(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
+                    lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512));
       }
     }
   }
@@ -283,15 +297,13 @@ struct StreamItem {
     }
   }
 
-  // Wait until the weights of the stage about to be used have landed (at most
-  // `pending` later stages of PER loads each in flight; the stage's activation
-  // rows were issued before its weights), make the weights readable, then meet
-  // the other waves.
-  __device__ __forceinline__ static void stage_wait(int pending, v4i (&w)[KG][NBW]) {
-    if (pending <= 0) wait_vm<0>();
-    else if (pending == 1 || D == 2) wait_vm<PER>();
-    else if (pending == 2 || D == 3) wait_vm<2 * PER>();
-    else wait_vm<(D - 1) * PER>();
+  // Wait until the weights of the stage about to be used have landed: every
+  // stage issues its loads (stages past the end re-read the last one), so
+  // exactly D-1 later stages of PER loads each may still be in flight; the
+  // stage's activation rows were issued before its weights.  Then make the
+  // weights readable and meet the other waves.
+  __device__ __forceinline__ static void stage_wait(v4i (&w)[KG][NBW]) {
+    wait_vm<(D - 1) * PER>();
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
@@ -335,57 +347,69 @@ struct StreamItem {
       for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
     v4i wr[D][KG][NBW];
 
+    // Every stage issues its loads, clamped to the last stage (L2 hits, never
+    // used), so each wait is the same constant; the loop body is D whole
+    // stages and the last S % D stages follow it, so no control-flow path
+    // skips a stage and then runs a later one.
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      if (s < S) {
-        if ((s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s * KG / SC, R);
-        issue_x(xt, xo, lds + (s % NX) * XSLOT, G, s);
-        load_w(wr[s], wt, wo, gbase + s * KG, G);
-      }
+      if (s < S && (s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s * KG / SC, R);
+      issue_x(xt, xo, lds + (s % NX) * XSLOT, G, min(s, S - 1));
+      load_w(wr[s], wt, wo, gbase + min(s, S - 1) * KG, G);
     }
 
-    for (int s0 = 0; s0 < S; s0 += D) {
+    auto stage = [&](int s, int u) __attribute__((always_inline)) {
+      stage_wait(wr[u]);
+      const int sn = s + D;
+      if (sn < S && (sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
+      issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, min(sn, S - 1));
+      const uint8_t* slot = lds + (s % NX) * XSLOT;
 #pragma unroll
-      for (int u = 0; u < D; ++u) {
-        const int s = s0 + u;
-        if (s < S) {
-          stage_wait(min(D - 1, S - 1 - s), wr[u]);
-          const int sn = s + D;
-          if (sn < S) {
-            if ((sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
-            issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, sn);
+      for (int kg = 0; kg < KG; ++kg) {
+        const int gl = s * KG + kg;  // group index within this wave's half
+        if (gl < gcount) {
+          const uint8_t* sbb = lds + P1_SB + ((gl / SC) & 1) * P1_SBBUF;
+          const uint8_t* sab = lds + P1_SA + ((gl / SC) & 1) * P1_SABUF;
+          const int gg = gl % SC;
+          int sbv[NBW];
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int col = (wn * NBW + j) * 16 + r16;
+            sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
           }
-          const uint8_t* slot = lds + (s % NX) * XSLOT;
 #pragma unroll
-          for (int kg = 0; kg < KG; ++kg) {
-            const int gl = s * KG + kg;  // group index within this wave's half
-            if (gl < gcount) {
-              const uint8_t* sbb = lds + P1_SB + ((gl / SC) & 1) * P1_SBBUF;
-              const uint8_t* sab = lds + P1_SA + ((gl / SC) & 1) * P1_SABUF;
-              const int gg = gl % SC;
-              int sbv[NBW];
+          for (int i = 0; i < MB; ++i) {
+            const int m = i * 16 + r16;
+            const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
+            const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
+            const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
+            const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
 #pragma unroll
-              for (int j = 0; j < NBW; ++j) {
-                const int col = (wn * NBW + j) * 16 + r16;
-                sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
-              }
-#pragma unroll
-              for (int i = 0; i < MB; ++i) {
-                const int m = i * 16 + r16;
-                const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
-                const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
-                const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
-                const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
-#pragma unroll
-                for (int j = 0; j < NBW; ++j)
-                  promote(acc[j][i], sa, mfma_group(wr[u][kg][j], x0, x1, sbv[j]));
-              }
-            }
+            for (int j = 0; j < NBW; ++j)
+              promote(acc[j][i], sa, mfma_group(wr[u][kg][j], x0, x1, sbv[j]));
           }
-          if (sn < S) load_w(wr[u], wt, wo, gbase + sn * KG, G);
         }
       }
+      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G);
+    };
+
+    static_assert(D == 2, "the stage loop below is written for two stages in flight");
+    int s0 = 0;
+    for (; s0 + 2 <= S; s0 += 2) {
+      stage(s0, 0);
+      stage(s0 + 1, 1);
     }
+    if (s0 < S) stage(s0, 0);
+    // the clamped trailing loads have landed; the ties keep their registers
+    // reserved until here (a value never read would otherwise be reused
+    // while its load is still in flight)
+    wait_vm<0>();
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) tie(wr[u][kg][j]);
 
     // add the two K halves in LDS (nothing is in flight -- the last wait was
     // for zero -- and every wave is past its last LDS read after this barrier)
@@ -456,7 +480,7 @@ __device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
 // straight into that wave's MFMA operand registers (the next group's weights
 // load while the current group's are in use); only the activation rows and
 // the scales, which every wave needs, are staged in LDS:
-//   X ring   : P2_NX slots x [128 rows][128 B]  (row chunk c at c ^ (row & 7))
+//   X ring   : P2_NX slots x [128 rows][128 B]  (row chunk c at c ^ key(row))
 //   SB chunk : 2 x [512 cols][SC] u32  (E8M0 codes of groups SC*c .. SC*c+3)
 //   SA chunk : 2 x [128 rows][SC] fp32
 // Stage s (one K group): wait (weights of group s and, older, its activation
@@ -483,27 +507,10 @@ constexpr int P2_SABUF = MF_BM * SC * 4;  // 2 KB
 constexpr int P2_BYTES = P2_SA + 2 * P2_SABUF;
 constexpr int P2_X_OPS = 2;             // activation loads per wave per stage
 constexpr int P2_W_OPS = 4;             // weight loads per wave per stage
-constexpr int P2_WAIT_MAX = P2_X_OPS + (P2_DW - 1) * (P2_X_OPS + P2_W_OPS);
 // a scale buffer is refilled P2_DX stages ahead, after every stage of the
 // chunk two back has passed the barrier of the stage that refills it
 static_assert(P2_DX <= SC, "scale chunk reuse distance");
 static_assert(P2_DW == 1, "the stage loop is unrolled for two weight slots");
-
-// Vector-memory ops this wave issues after the weights of stage s (scale
-// chunks not counted, which only makes the wait stricter).  Iteration t
-// issues W(t + P2_DW) and then X(t + P2_DX); the prologue is iterations
-// -P2_DX .. -1 under the same rule.
-__device__ __forceinline__ int p2_ops_after_w(int s, int G) {
-  const int t0 = s - P2_DW;
-  int n = (t0 + P2_DX < G) ? P2_X_OPS : 0;
-#pragma unroll
-  for (int d = 1; d < P2_DW; ++d) {
-    const int t = t0 + d;
-    if (t + P2_DW < G) n += P2_W_OPS;
-    if (t + P2_DX < G) n += P2_X_OPS;
-  }
-  return n;
-}
 
 // Activation rows of group g: 128 rows x 128 B, two 8-row loads per wave
 // (xt = the tile's first row, xo = this lane's byte offsets from it).
@@ -521,16 +528,16 @@ __device__ __forceinline__ void p2_issue_scales(const GemmArgs& p, uint8_t* lds,
                                                 int rows, int n0, int c, int R) {
   const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
   const int K = p.K, N = p.N, G = K >> 7;
-  const int gg = lane & 3;
-  const int g = min(SC * c + gg, G - 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // [col][gg]
+    const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // rows [col] of SC words
+    const int g = min(SC * c + ((lane & 3) ^ skey<SC>(col)), G - 1);
     const int n = min(n0 + col, N - 1);
     vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
             lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
   }
-  const int r = (wave * 64 + lane) >> 2;  // [row][gg]
+  const int r = (wave * 64 + lane) >> 2;  // rows [row] of SC words
+  const int g = min(SC * c + ((lane & 3) ^ skey<SC>(r)), G - 1);
   const size_t row = (size_t)row0 + min(r, rows - 1);
   vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P2_SA + (c & 1) * P2_SABUF + wave * 256));
 }
@@ -545,23 +552,26 @@ __device__ __forceinline__ void p2_load_w(v4i (&w)[4], const uint8_t* wt, const 
 
 // LDS addresses of this lane's fragments in a stage slot / scale buffer: row
 // block mi adds the immediate mi * 2048 (X) or mi * 256 (SA).  Row m = 16 mi
-// + i has swizzle key m & 7 = i & 7 for every mi.
+// + i has activation key xkey(m) = xkey(i) for every mi, and scale key
+// skey<SC>(m) = ((2 mi) & 3) ^ (i >> 3): one scale address for even mi, one
+// for odd.
 struct P2Lds {
-  const uint8_t* x0;  // chunk q of row i
-  const uint8_t* x1;  // chunk q + 4 of row i
-  const uint8_t* sa;  // scale (row i, group gg)
+  const uint8_t* x0;   // chunk q of row i
+  const uint8_t* x1;   // chunk q + 4 of row i
+  const uint8_t* sa0;  // scale (row i, group gg), even mi
+  const uint8_t* sa1;  // odd mi
 };
 
 __device__ __forceinline__ void p2_read_x(const P2Lds& a, int mi, v4i& x0, v4i& x1, float& sa) {
   x0 = lds128(a.x0 + mi * 2048);
   x1 = lds128(a.x1 + mi * 2048);
-  sa = ldsf(a.sa + mi * 16 * SC * 4);
+  sa = ldsf(((mi & 1) ? a.sa1 : a.sa0) + mi * 16 * SC * 4);
 }
 
 // One K group for NMB row blocks.  Step mi issues the LDS reads of block
-// mi+1, the promotion of the previous step's partials (carried across stages
-// in prev/sprev, so the first step of a stage has arithmetic to do while its
-// reads are in flight) and the four MFMAs of block mi; the scheduling fences
+// mi+1, the four MFMAs of block mi and the promotion of the previous step's
+// partials (carried across stages in prev/sprev, so the first step of a stage
+// has arithmetic to do while its reads are in flight); the scheduling fences
 // keep each step's work together.
 template <int NMB>
 __device__ __forceinline__ void p2_group(v4f (&acc)[8][4], v4f (&prev)[4], float& sprev, const v4i (&w)[4],
@@ -576,14 +586,25 @@ __device__ __forceinline__ void p2_group(v4f (&acc)[8][4], v4f (&prev)[4], float
     if (mi + 1 < NMB) p2_read_x(a, mi + 1, xb0, xb1, sab_n);
     // the previous step's block: the last block of the previous group when mi == 0
     const int pm = mi == 0 ? NMB - 1 : mi - 1;
+    v4f pn[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) pn[nb] = mfma_group(w[nb], xa0, xa1, sbv[nb]);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) promote(acc[pm][nb], sprev, prev[nb]);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) prev[nb] = mfma_group(w[nb], xa0, xa1, sbv[nb]);
+    for (int nb = 0; nb < 4; ++nb) prev[nb] = pn[nb];
     sprev = saa;
     xa0 = xb0;
     xa1 = xb1;
     saa = sab_n;
+    // step order: the next block's LDS reads, then each MFMA followed by four
+    // of the promotions, which run while the matrix core works
+    if (mi + 1 < NMB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -618,7 +639,7 @@ struct MfmaTile {
 #pragma unroll
     for (int i = 0; i < P2_X_OPS; ++i) {
       const int r = (wave * P2_X_OPS + i) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
+      const int c = (lane & 7) ^ xkey(r);
       xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
     }
 #pragma unroll
@@ -627,24 +648,26 @@ struct MfmaTile {
       wo[nb] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
     }
     // LDS byte offsets of this lane's activation fragments within a slot
-    xl0 = r16 * 128 + ((q ^ (r16 & 7)) << 4);
-    xl1 = r16 * 128 + (((q + 4) ^ (r16 & 7)) << 4);
+    xl0 = r16 * 128 + ((q ^ xkey(r16)) << 4);
+    xl1 = r16 * 128 + (((q + 4) ^ xkey(r16)) << 4);
   }
 
-  // loads of iteration t of the issue rule: W(t + P2_DW) into wnext, X(t + P2_DX)
+  // loads of iteration t of the issue rule: W(t + P2_DW) into wnext, then
+  // X(t + P2_DX), both clamped to the last group (past the end they re-read it:
+  // L2 hits, never used), so every stage issues the same loads
   __device__ __forceinline__ void issue(int t, v4i (&wnext)[4]) {
     const int sw = t + P2_DW;
-    if (sw >= 0 && sw < G) p2_load_w(wnext, wt, wo, sw);
+    if (sw >= 0) p2_load_w(wnext, wt, wo, min(sw, G - 1));
     const int sx = t + P2_DX;
-    if (sx < G) {
-      if (sx % SC == 0) p2_issue_scales(p, lds, e, row0, rows, n0, sx / SC, R);
-      p2_issue_x(xt, xo, lds + (sx % P2_NX) * P2_XSLOT, sx);
-    }
+    if (sx < G && sx % SC == 0) p2_issue_scales(p, lds, e, row0, rows, n0, sx / SC, R);
+    p2_issue_x(xt, xo, lds + (sx % P2_NX) * P2_XSLOT, min(sx, G - 1));
   }
 
+  // the weights of stage s and (issued before them) its activation rows have
+  // landed once at most the P2_X_OPS newest loads are in flight
   __device__ __forceinline__ void stage(int s, v4i (&wcur)[4], v4i (&wnext)[4], v4f (&acc)[8][4],
                                         v4f (&prev)[4], float& sprev) {
-    wait_vm_at_most<P2_WAIT_MAX, 2>(p2_ops_after_w(s, G));
+    wait_vm<P2_X_OPS>();
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) tie(wcur[nb]);
     wg_barrier();
@@ -655,13 +678,18 @@ struct MfmaTile {
       const uint8_t* sab = lds + P2_SA + ((s / SC) & 1) * P2_SABUF;
       const int gg = s % SC;
       int sbv[4];
-      const uint8_t* sbl = sbb + ((wn * 64 + r16) * SC + gg) * 4;
+      // column wn*64 + 16 nb + r16 has scale key ((2 nb) & 3) ^ (r16 >> 3)
+      const int k0 = gg ^ (r16 >> 3);
+      const uint8_t* sbl0 = sbb + ((wn * 64 + r16) * SC + k0) * 4;
+      const uint8_t* sbl1 = sbb + ((wn * 64 + r16) * SC + (k0 ^ 2)) * 4;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sbv[nb] = (int)((lds32(sbl + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
+      for (int nb = 0; nb < 4; ++nb)
+        sbv[nb] = (int)((lds32(((nb & 1) ? sbl1 : sbl0) + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
       P2Lds a;
       a.x0 = slot + xl0;
       a.x1 = slot + xl1;
-      a.sa = sab + (r16 * SC + gg) * 4;
+      a.sa0 = sab + (r16 * SC + k0) * 4;
+      a.sa1 = sab + (r16 * SC + (k0 ^ 2)) * 4;
       p2_group<NMB>(acc, prev, sprev, wcur, a, sbv);
     }
   }
@@ -691,9 +719,21 @@ struct MfmaTile {
     // prologue = iterations -P2_DX .. -1 of the issue rule; W(0) lands in w0
     issue(-2, w1);
     issue(-1, w0);
-    for (int s = 0; s < G; s += 2) {
+    // whole pairs of stages, then the last odd one: no control-flow path
+    // skips a stage and then runs a later one
+    int s = 0;
+    for (; s + 2 <= G; s += 2) {
       stage(s, w0, w1, acc, prev, sprev);
-      if (s + 1 < G) stage(s + 1, w1, w0, acc, prev, sprev);
+      stage(s + 1, w1, w0, acc, prev, sprev);
+    }
+    if (s < G) stage(s, w0, w1, acc, prev, sprev);
+    // the clamped trailing loads have landed; the ties keep their registers
+    // reserved until here
+    wait_vm<0>();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      tie(w0[nb]);
+      tie(w1[nb]);
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) promote(acc[NMB - 1][nb], sprev, prev[nb]);
