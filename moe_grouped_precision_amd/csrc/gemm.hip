@@ -90,21 +90,22 @@ __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
-// 16 bytes per lane from sbase + voff (sbase wave-uniform) to LDS at
-// lds + 16 * lane (lds wave-uniform; lanes outside exec write nothing).
-__device__ __forceinline__ void vm_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+// Loads that a stage issues past the end of the K loop run with exec = 0: the
+// instruction still issues and counts toward vmcnt (so every wait stays one
+// constant) but reads no memory and writes no register.  `mask` is the exec
+// mask to load with: live_mask(true) = the current exec, live_mask(false) = 0.
+__device__ __forceinline__ uint64_t live_mask(bool live) {
+  return live ? __builtin_amdgcn_read_exec() : 0ull;
 }
-// The same for lanes 0-31 only (lds + 16 * lane, 512 bytes): the asm masks the
-// upper half of exec itself, so the load is one straight-line instruction that
-// every wave issues, not a branch around it.
-__device__ __forceinline__ void vm_dma16_lo(const void* sbase, uint32_t voff, uint32_t lds) {
+
+// 16 bytes per lane from sbase + voff (sbase wave-uniform) to LDS at
+// lds + 16 * lane (lds wave-uniform; lanes outside mask write nothing).
+__device__ __forceinline__ void vm_dma16(const void* sbase, uint32_t voff, uint32_t lds, uint64_t mask) {
   uint64_t saved;
-  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b32 exec_hi, 0\n\ts_mov_b32 m0, %3\n\ts_nop 3\n\t"
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %4\n\ts_mov_b32 m0, %3\n\ts_nop 3\n\t"
                "global_load_lds_dwordx4 %1, %2\n\ts_mov_b64 exec, %0"
                : "=&s"(saved)
-               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(mask)
                : "memory", "m0", "exec");
 }
 // 4 bytes per lane from a per-lane address to LDS at lds + 4 * lane.
@@ -112,16 +113,27 @@ __device__ __forceinline__ void vm_dma4(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(addr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
-// 16 bytes per lane into registers; the value may be read only after a wait
-// that covers this load, followed by tie() on the register.
-__device__ __forceinline__ v4i vm_load16(const void* sbase, uint32_t voff) {
+// 16 bytes per lane into registers (lanes outside mask load nothing); the
+// value may be read only after a wait that covers this load, followed by tie()
+// on the register.  _nt marks the data nontemporal (streamed once).
+__device__ __forceinline__ v4i vm_load16(const void* sbase, uint32_t voff, uint64_t mask) {
   v4i r;
-  asm volatile("s_nop 4\n\tglobal_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)));
+  uint64_t saved;
+  asm volatile("s_mov_b64 %1, exec\n\ts_mov_b64 exec, %4\n\ts_nop 4\n\t"
+               "global_load_dwordx4 %0, %2, %3\n\ts_mov_b64 exec, %1"
+               : "=v"(r), "=&s"(saved)
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(mask)
+               : "exec");
   return r;
 }
-__device__ __forceinline__ v4i vm_load16_nt(const void* sbase, uint32_t voff) {
+__device__ __forceinline__ v4i vm_load16_nt(const void* sbase, uint32_t voff, uint64_t mask) {
   v4i r;
-  asm volatile("s_nop 4\n\tglobal_load_dwordx4 %0, %1, %2 nt" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)));
+  uint64_t saved;
+  asm volatile("s_mov_b64 %1, exec\n\ts_mov_b64 exec, %4\n\ts_nop 4\n\t"
+               "global_load_dwordx4 %0, %2, %3 nt\n\ts_mov_b64 exec, %1"
+               : "=v"(r), "=&s"(saved)
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(mask)
+               : "exec");
   return r;
 }
 __device__ __forceinline__ void tie(v4i& r) { asm volatile("" : "+v"(r)); }
@@ -244,9 +256,10 @@ struct StreamItem {
   // Activation rows of stage s: 8*MB loads of 4 rows x 128 B per group, MB per
   // wave (half a wave each).  xt = the item's first row.
   __device__ __forceinline__ static void issue_x(const uint8_t* xt, const uint32_t (&xo)[MB], uint8_t* slot,
-                                                 int G, int s) {
-    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+                                                 int G, int s, bool live) {
+    const int wave = uniform(threadIdx.x >> 6);
     const int Gh = (G + 1) / 2;
+    const uint64_t mask = live_mask(live) & 0xffffffffull;  // lanes 0-31 load
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const int g0 = min(s * KG + kg, G - 1), g1 = min(Gh + s * KG + kg, G - 1);
@@ -254,8 +267,8 @@ struct StreamItem {
       for (int i = 0; i < MB; ++i) {
         const int jx = wave * MB + i;
         const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
-        vm_dma16_lo(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
-                    lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512));
+        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
+                 lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512), mask);
       }
     }
   }
@@ -288,17 +301,18 @@ struct StreamItem {
   // Weight fragments of this wave for the stage starting at group gfirst
   // (16 B per lane per 16-column block and group).  wt = the item's first column.
   __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt,
-                                                const uint32_t (&wo)[NBW], int gfirst, int G) {
+                                                const uint32_t (&wo)[NBW], int gfirst, int G, bool live) {
+    const uint64_t mask = live_mask(live);
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const uint8_t* wg = wt + (size_t)min(gfirst + kg, G - 1) * 64;
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) w[kg][j] = vm_load16_nt(wg, wo[j]);
+      for (int j = 0; j < NBW; ++j) w[kg][j] = vm_load16_nt(wg, wo[j], mask);
     }
   }
 
   // Wait until the weights of the stage about to be used have landed: every
-  // stage issues its loads (stages past the end re-read the last one), so
+  // stage issues its loads (those past the end with exec = 0), so
   // exactly D-1 later stages of PER loads each may still be in flight; the
   // stage's activation rows were issued before its weights.  Then make the
   // weights readable and meet the other waves.
@@ -347,22 +361,22 @@ struct StreamItem {
       for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
     v4i wr[D][KG][NBW];
 
-    // Every stage issues its loads, clamped to the last stage (L2 hits, never
-    // used), so each wait is the same constant; the loop body is D whole
-    // stages and the last S % D stages follow it, so no control-flow path
-    // skips a stage and then runs a later one.
+    // Every stage issues its loads (past the last stage with exec = 0 and
+    // addresses clamped in range), so each wait is the same constant; the loop
+    // body is D whole stages and the last S % D stages follow it, so no
+    // control-flow path skips a stage and then runs a later one.
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       if (s < S && (s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s * KG / SC, R);
-      issue_x(xt, xo, lds + (s % NX) * XSLOT, G, min(s, S - 1));
-      load_w(wr[s], wt, wo, gbase + min(s, S - 1) * KG, G);
+      issue_x(xt, xo, lds + (s % NX) * XSLOT, G, min(s, S - 1), s < S);
+      load_w(wr[s], wt, wo, gbase + min(s, S - 1) * KG, G, s < S);
     }
 
     auto stage = [&](int s, int u) __attribute__((always_inline)) {
       stage_wait(wr[u]);
       const int sn = s + D;
       if (sn < S && (sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
-      issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, min(sn, S - 1));
+      issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, min(sn, S - 1), sn < S);
       const uint8_t* slot = lds + (s % NX) * XSLOT;
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
@@ -390,7 +404,7 @@ struct StreamItem {
           }
         }
       }
-      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G);
+      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G, sn < S);
     };
 
     static_assert(D == 2, "the stage loop below is written for two stages in flight");
@@ -400,9 +414,9 @@ struct StreamItem {
       stage(s0 + 1, 1);
     }
     if (s0 < S) stage(s0, 0);
-    // the clamped trailing loads have landed; the ties keep their registers
-    // reserved until here (a value never read would otherwise be reused
-    // while its load is still in flight)
+    // every load has retired; the ties keep the ring registers reserved until
+    // here (a value never read would otherwise be reused while its load is
+    // still in flight)
     wait_vm<0>();
 #pragma unroll
     for (int u = 0; u < D; ++u)
@@ -515,11 +529,13 @@ static_assert(P2_DW == 1, "the stage loop is unrolled for two weight slots");
 // Activation rows of group g: 128 rows x 128 B, two 8-row loads per wave
 // (xt = the tile's first row, xo = this lane's byte offsets from it).
 __device__ __forceinline__ void p2_issue_x(const uint8_t* xt, const uint32_t (&xo)[P2_X_OPS],
-                                           uint8_t* slot, int g) {
+                                           uint8_t* slot, int g, bool live) {
   const int wave = uniform(threadIdx.x >> 6);
   const uint8_t* xg = xt + (size_t)g * 128;
+  const uint64_t mask = live_mask(live);
 #pragma unroll
-  for (int i = 0; i < P2_X_OPS; ++i) vm_dma16(xg, xo[i], lds_u32(slot + (wave * P2_X_OPS + i) * 1024));
+  for (int i = 0; i < P2_X_OPS; ++i)
+    vm_dma16(xg, xo[i], lds_u32(slot + (wave * P2_X_OPS + i) * 1024), mask);
 }
 
 // Scale chunk c: 512 columns x SC groups of E8M0 words (four loads per wave)
@@ -544,10 +560,12 @@ __device__ __forceinline__ void p2_issue_scales(const GemmArgs& p, uint8_t* lds,
 
 // Weights of group g for this wave's four 16-column blocks (wt = the tile's
 // first column, wo = this lane's byte offsets from it).
-__device__ __forceinline__ void p2_load_w(v4i (&w)[4], const uint8_t* wt, const uint32_t (&wo)[4], int g) {
+__device__ __forceinline__ void p2_load_w(v4i (&w)[4], const uint8_t* wt, const uint32_t (&wo)[4], int g,
+                                          bool live) {
   const uint8_t* wg = wt + (size_t)g * 64;
+  const uint64_t mask = live_mask(live);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) w[nb] = vm_load16(wg, wo[nb]);
+  for (int nb = 0; nb < 4; ++nb) w[nb] = vm_load16(wg, wo[nb], mask);
 }
 
 // LDS addresses of this lane's fragments in a stage slot / scale buffer: row
@@ -653,14 +671,14 @@ struct MfmaTile {
   }
 
   // loads of iteration t of the issue rule: W(t + P2_DW) into wnext, then
-  // X(t + P2_DX), both clamped to the last group (past the end they re-read it:
-  // L2 hits, never used), so every stage issues the same loads
+  // X(t + P2_DX); past the last group they issue with exec = 0 (addresses
+  // clamped in range), so every stage issues the same number of loads
   __device__ __forceinline__ void issue(int t, v4i (&wnext)[4]) {
     const int sw = t + P2_DW;
-    if (sw >= 0) p2_load_w(wnext, wt, wo, min(sw, G - 1));
+    if (sw >= 0) p2_load_w(wnext, wt, wo, min(sw, G - 1), sw < G);
     const int sx = t + P2_DX;
     if (sx < G && sx % SC == 0) p2_issue_scales(p, lds, e, row0, rows, n0, sx / SC, R);
-    p2_issue_x(xt, xo, lds + (sx % P2_NX) * P2_XSLOT, min(sx, G - 1));
+    p2_issue_x(xt, xo, lds + (sx % P2_NX) * P2_XSLOT, min(sx, G - 1), sx < G);
   }
 
   // the weights of stage s and (issued before them) its activation rows have
@@ -727,9 +745,7 @@ struct MfmaTile {
       stage(s + 1, w1, w0, acc, prev, sprev);
     }
     if (s < G) stage(s, w0, w1, acc, prev, sprev);
-    // the clamped trailing loads have landed; the ties keep their registers
-    // reserved until here
-    wait_vm<0>();
+    wait_vm<0>();  // every load has retired; the ties keep their registers reserved until here
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       tie(w0[nb]);
