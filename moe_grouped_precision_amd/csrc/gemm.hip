@@ -252,6 +252,7 @@ struct StreamItem {
   // a scale chunk buffer is reloaded D stages before the first stage of the
   // chunk after next: every stage of the chunk before must be done by then
   static_assert(SC % KG == 0 && D * KG <= SC, "scale chunk reuse distance");
+  static_assert(KG == 2, "a stage's weight loads cover one 128-byte line (two groups) per column");
 
   // Activation rows of stage s: 8*MB loads of 4 rows x 128 B per group, MB per
   // wave (half a wave each).  xt = the item's first row.
@@ -298,16 +299,35 @@ struct StreamItem {
     }
   }
 
-  // Weight fragments of this wave for the stage starting at group gfirst
-  // (16 B per lane per 16-column block and group).  wt = the item's first column.
+  // Weights of this wave for the stage whose groups are gfirst, gfirst + 1:
+  // per 16-column block j, load w[h][j] covers columns 8h .. 8h+7 of the block
+  // with one full 128-byte line (both groups) per column, lane 16q + i reading
+  // column 8h + (i & 7), group gfirst + (i >> 3), bytes 16q .. 16q+15.  Whole
+  // lines per request stream from HBM at the rate of contiguous reads; two
+  // 64-byte requests per line (one per group) do not.  pair_operands() turns
+  // the two loads into the MFMA operands of the two groups.  wt = the item's
+  // first column; wo = this lane's column offsets; goff = its group offset
+  // (the second group is clamped to the last one when G is odd).
   __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt,
-                                                const uint32_t (&wo)[NBW], int gfirst, int G, bool live) {
+                                                const uint32_t (&wo)[2][NBW], int gfirst, int G, bool live) {
     const uint64_t mask = live_mask(live);
+    const uint32_t goff = (uint32_t)min(gfirst + ((threadIdx.x & 15) >> 3), G - 1) * 64u;
 #pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      const uint8_t* wg = wt + (size_t)min(gfirst + kg, G - 1) * 64;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) w[kg][j] = vm_load16_nt(wg, wo[j], mask);
+      for (int j = 0; j < NBW; ++j) w[h][j] = vm_load16_nt(wt, wo[h][j] + goff, mask);
+  }
+
+  // MFMA operand of group gfirst + g of block j: lane 16q + i needs column i,
+  // bytes 16q.. of that group.  Load h holds it in lane 16q + (i & 7) + 8g
+  // when i >> 3 == h, so the operand is load g's own lanes in one half of each
+  // 16-lane row and the other load's lanes rotated by 8 in the other half.
+  __device__ __forceinline__ static void pair_operands(const v4i& a, const v4i& b, v4i& g0, v4i& g1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // row_ror:8 (dpp_ctrl 0x128); bank_mask picks the 4-lane banks written
+      g0[d] = __builtin_amdgcn_update_dpp(a[d], b[d], 0x128, 0xf, 0xc, false);
+      g1[d] = __builtin_amdgcn_update_dpp(b[d], a[d], 0x128, 0xf, 0x3, false);
     }
   }
 
@@ -347,12 +367,14 @@ struct StreamItem {
       xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
     }
     const uint8_t* wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
-    uint32_t wo[NBW];
+    uint32_t wo[2][NBW];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int n = min(n0 + (wn * NBW + j) * 16 + r16, N - 1);
-      wo[j] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int n = min(n0 + (wn * NBW + j) * 16 + 8 * h + (r16 & 7), N - 1);
+        wo[h][j] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
+      }
 
     v4f acc[NBW][MB];
 #pragma unroll
@@ -378,6 +400,9 @@ struct StreamItem {
       if (sn < S && (sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
       issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, min(sn, S - 1), sn < S);
       const uint8_t* slot = lds + (s % NX) * XSLOT;
+      v4i wop[KG][NBW];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) pair_operands(wr[u][0][j], wr[u][1][j], wop[0][j], wop[1][j]);
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         const int gl = s * KG + kg;  // group index within this wave's half
@@ -400,7 +425,7 @@ struct StreamItem {
             const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
-              promote(acc[j][i], sa, mfma_group(wr[u][kg][j], x0, x1, sbv[j]));
+              promote(acc[j][i], sa, mfma_group(wop[kg][j], x0, x1, sbv[j]));
           }
         }
       }
