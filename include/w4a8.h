@@ -67,6 +67,7 @@ enum {
 /* Limits of this version. */
 #define W4A8_MAX_EXPERTS 1024
 #define W4A8_MAX_K 1048576     /* keeps every in-tile byte offset within 32 bits */
+#define W4A8_MAX_N 16777216    /* keeps work-item counts within 32 bits */
 
 /*
  * w4a8_route_prep -- routing histogram, exclusive-scan offsets and row map.
@@ -134,7 +135,7 @@ int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K,
  * C_bf16_dev         out uint16 (bf16 bits) [R][N]; only rows < R are written.
  *                    16-byte aligned.
  * Limits: 1 <= E <= W4A8_MAX_EXPERTS; K % 128 == 0, 128 <= K <= W4A8_MAX_K;
- * N % 32 == 0, N >= 32; R*K and R*N below 2^62.  A, a_scales and C must hold R rows.
+ * N % 32 == 0, 32 <= N <= W4A8_MAX_N; R*K and R*N below 2^62.  A, a_scales and C must hold R rows.
  * Numerics: each 128-K group is reduced by a scaled MFMA in fp32 (E8M0 weight
  * scales applied inside it), multiplied by its fp32 activation scale and
  * accumulated in fp32; one RNE rounding to bf16 at the end.  NaN codes

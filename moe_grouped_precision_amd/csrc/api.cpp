@@ -73,7 +73,8 @@ int check_gemm_shape(int E, int N, int K) {
   if (E < 1 || E > W4A8_MAX_EXPERTS) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_EXPERTS);
   if (K < 128 || K % 128 || K > W4A8_MAX_K)
     return fail(W4A8_ERR_SHAPE, "K=%d must be a multiple of 128 in [128, %d]", K, W4A8_MAX_K);
-  if (N < 32 || N % 32) return fail(W4A8_ERR_SHAPE, "N=%d must be a positive multiple of 32", N);
+  if (N < 32 || N % 32 || N > W4A8_MAX_N)
+    return fail(W4A8_ERR_SHAPE, "N=%d must be a multiple of 32 in [32, %d]", N, W4A8_MAX_N);
   return W4A8_OK;
 }
 

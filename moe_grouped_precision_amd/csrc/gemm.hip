@@ -113,28 +113,27 @@ __device__ __forceinline__ void vm_dma4(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(addr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
-// 16 bytes per lane into registers (lanes outside mask load nothing); the
-// value may be read only after a wait that covers this load, followed by tie()
-// on the register.  _nt marks the data nontemporal (streamed once).
-__device__ __forceinline__ v4i vm_load16(const void* sbase, uint32_t voff, uint64_t mask) {
-  v4i r;
+// 16 bytes per lane into r (lanes outside mask load nothing); r may be read
+// only after a wait that covers this load, followed by tie() on it.  _nt
+// marks the data nontemporal (streamed once).  r is an input as well as the
+// output, so a ring slot reloaded in a loop is one live range in one
+// register: the compiler never moves a slot between registers (a copy of a
+// register whose load is still in flight would copy stale data).
+__device__ __forceinline__ void vm_load16(v4i& r, const void* sbase, uint32_t voff, uint64_t mask) {
   uint64_t saved;
   asm volatile("s_mov_b64 %1, exec\n\ts_mov_b64 exec, %4\n\ts_nop 4\n\t"
                "global_load_dwordx4 %0, %2, %3\n\ts_mov_b64 exec, %1"
-               : "=v"(r), "=&s"(saved)
+               : "+v"(r), "=&s"(saved)
                : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(mask)
                : "exec");
-  return r;
 }
-__device__ __forceinline__ v4i vm_load16_nt(const void* sbase, uint32_t voff, uint64_t mask) {
-  v4i r;
+__device__ __forceinline__ void vm_load16_nt(v4i& r, const void* sbase, uint32_t voff, uint64_t mask) {
   uint64_t saved;
   asm volatile("s_mov_b64 %1, exec\n\ts_mov_b64 exec, %4\n\ts_nop 4\n\t"
                "global_load_dwordx4 %0, %2, %3 nt\n\ts_mov_b64 exec, %1"
-               : "=v"(r), "=&s"(saved)
+               : "+v"(r), "=&s"(saved)
                : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(mask)
                : "exec");
-  return r;
 }
 __device__ __forceinline__ void tie(v4i& r) { asm volatile("" : "+v"(r)); }
 
@@ -315,7 +314,7 @@ struct StreamItem {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) w[h][j] = vm_load16_nt(wt, wo[h][j] + goff, mask);
+      for (int j = 0; j < NBW; ++j) vm_load16_nt(w[h][j], wt, wo[h][j] + goff, mask);
   }
 
   // MFMA operand of group gfirst + g of block j: lane 16q + i needs column i,
@@ -382,6 +381,12 @@ struct StreamItem {
 #pragma unroll
       for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
     v4i wr[D][KG][NBW];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) wr[u][kg][j] = v4i{0, 0, 0, 0};
 
     // Every stage issues its loads (past the last stage with exec = 0 and
     // addresses clamped in range), so each wait is the same constant; the loop
@@ -590,7 +595,7 @@ __device__ __forceinline__ void p2_load_w(v4i (&w)[4], const uint8_t* wt, const 
   const uint8_t* wg = wt + (size_t)g * 64;
   const uint64_t mask = live_mask(live);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) w[nb] = vm_load16(wg, wo[nb], mask);
+  for (int nb = 0; nb < 4; ++nb) vm_load16(w[nb], wg, wo[nb], mask);
 }
 
 // LDS addresses of this lane's fragments in a stage slot / scale buffer: row
@@ -758,6 +763,8 @@ struct MfmaTile {
     float sprev = 0.f;
     asm volatile("" : "+v"(sprev));
     v4i w0[4], w1[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) w0[nb] = w1[nb] = v4i{0, 0, 0, 0};
 
     // prologue = iterations -P2_DX .. -1 of the issue rule; W(0) lands in w0
     issue(-2, w1);

@@ -104,54 +104,92 @@ __device__ inline uint32_t bf16_rne(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Inclusive sum / max over the 64 lanes of a wave: DPP row shifts inside each
+// 16-lane row, then the row broadcasts of lane 15 and lane 31 across rows.
+// Disabled lanes and lanes without a source read 0 (the `old` operand), which
+// is neutral for sums and for maxima of non-negative values.
+// ---------------------------------------------------------------------------
+__device__ inline int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+__device__ inline int wave_max_nonneg(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// ---------------------------------------------------------------------------
 // Plan prologue run by every GEMM workgroup: offsets into LDS, validity check,
-// and the exclusive scans of the m-tile counts of both classes.
+// and the exclusive scans of the m-tile counts of both classes.  Wave 0 does
+// the work (lane l owns a contiguous run of experts); the other waves wait at
+// one barrier.
 //   s_off[0..E]    expert offsets
 //   s_sbase[0..E]  first streaming-class m-tile of each expert; [E] = total
 //   s_mbase[0..E]  first MFMA-class m-tile of each expert;      [E] = total
+//   s_info[0]      nonzero if the offsets are invalid
+//   s_info[1]      row blocks (GRAN rows) of the largest streaming tile
 // Returns false (uniformly across the block) if the offsets are invalid.
 // ---------------------------------------------------------------------------
 __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int* s_off,
-                                     int* s_sbase, int* s_mbase, int* s_wave) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i <= E; i += blockDim.x) s_off[i] = offsets[i];
-  __syncthreads();
-  int bad = 0;
-  for (int i = tid; i < E; i += blockDim.x) bad |= (s_off[i + 1] < s_off[i]);
-  if (tid == 0) bad |= (s_off[0] != 0);
-  bad = __syncthreads_or(bad);
-  if (bad) return false;
-  // each thread owns a contiguous run of experts
-  const int per = (E + blockDim.x - 1) / blockDim.x;
-  const int e0 = tid * per;
-  int ls = 0, lm = 0;
-  for (int i = 0; i < per; ++i) {
-    int e = e0 + i;
-    if (e < E) {
-      TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
-      ls += (t.cls == CLASS_STREAM) ? t.n_m : 0;
-      lm += (t.cls == CLASS_MFMA) ? t.n_m : 0;
+                                     int* s_sbase, int* s_mbase, int* s_info) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (E + 64) / 64;  // offsets per lane, so that 64 * per > E
+    const int i0 = lane * per;
+    int bad = 0, ls = 0, lm = 0, mb = 0;
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e <= E) {
+        const int a = offsets[e];
+        s_off[e] = a;
+        if (e == 0) bad |= a != 0;
+        if (e < E) {
+          const int b = offsets[e + 1];
+          bad |= b < a;
+          const TileChoice t = tile_rule(b - a);
+          if (t.cls == CLASS_STREAM) {
+            ls += t.n_m;
+            mb = max(mb, t.tile_m / GRAN);
+          }
+          if (t.cls == CLASS_MFMA) lm += t.n_m;
+        }
+      }
+    }
+    const bool any_bad = __ballot(bad != 0) != 0;
+    const int is = wave_inclusive_sum(ls), im = wave_inclusive_sum(lm);
+    const int mbmax = wave_max_nonneg(mb);
+    if (!any_bad) {
+      int rs = is - ls, rm = im - lm;
+      for (int k = 0; k < per; ++k) {
+        const int e = i0 + k;
+        if (e < E) {
+          s_sbase[e] = rs;
+          s_mbase[e] = rm;
+          const TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
+          rs += t.cls == CLASS_STREAM ? t.n_m : 0;
+          rm += t.cls == CLASS_MFMA ? t.n_m : 0;
+        }
+      }
+    }
+    if (lane == 0) {
+      s_sbase[E] = __builtin_amdgcn_readlane(is, 63);
+      s_mbase[E] = __builtin_amdgcn_readlane(im, 63);
+      s_info[0] = any_bad;
+      s_info[1] = mbmax;
     }
   }
-  int tot_s, tot_m;
-  int rs = block_exclusive_scan(ls, s_wave, &tot_s);
-  int rm = block_exclusive_scan(lm, s_wave, &tot_m);
-  for (int i = 0; i < per; ++i) {
-    int e = e0 + i;
-    if (e < E) {
-      s_sbase[e] = rs;
-      s_mbase[e] = rm;
-      TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
-      rs += (t.cls == CLASS_STREAM) ? t.n_m : 0;
-      rm += (t.cls == CLASS_MFMA) ? t.n_m : 0;
-    }
-  }
-  if (tid == 0) {
-    s_sbase[E] = tot_s;
-    s_mbase[E] = tot_m;
-  }
   __syncthreads();
-  return true;
+  return s_info[0] == 0;
 }
 
 // Expert owning class-local m-tile `mt`: the e with s_base[e] <= mt < s_base[e+1].

@@ -77,6 +77,7 @@ NUL = ctypes.c_void_p(0)
     ((P16, P16, 0, P16, P16, P16, 8, 256, 500, P16, NUL), 2),      # K % 128
     ((P16, P16, 0, P16, P16, P16, 8, 256, (1 << 20) + 128, P16, NUL), 2),  # K above the limit
     ((P16, P16, 0, P16, P16, P16, 8, 48, 512, P16, NUL), 2),       # N % 32
+    ((P16, P16, 0, P16, P16, P16, 8, (1 << 24) + 32, 512, P16, NUL), 2),  # N above the limit
     ((P16, P16, 2, P16, P16, P16, 8, 256, 512, P16, NUL), 3),      # bad layout
     ((NUL, P16, 0, P16, P16, P16, 8, 256, 512, P16, NUL), 1),      # null A
     ((P16, P16, 0, P16, P16, P16, 8, 256, 512, NUL, NUL), 1),      # null C
