@@ -20,6 +20,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw4a8.so")
 SOURCES = ["api.cpp", "prep.hip", "gemm.hip"]
+# roofline probes (sustained MFMA rate and HBM read bandwidth), a library of
+# their own: the benchmark loads them, the GEMM path does not
+PROBE_LIB = os.path.join(HERE, "libw4a8_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -73,33 +77,39 @@ def check_device_asm(cc: str, tmp: str, verbose: bool = False) -> None:
                                "\n".join(findings[:20]))
 
 
-def build(verbose: bool = False, debug: bool = False) -> str:
-    """Compile every source, check the device assembly of the inline-asm
-    kernels, and link libw4a8.so; returns the library path."""
-    cc = hipcc()
-    with tempfile.TemporaryDirectory(prefix="w4a8_build_") as tmp:
-        if not debug:
-            check_device_asm(cc, tmp, verbose)
-        objs = []
-        for src in SOURCES:
-            path = os.path.join(CSRC, src)
-            obj = os.path.join(tmp, src.replace(".", "_") + ".o")
-            cmd = [cc, "-x", "hip", *compile_flags(debug), "-c", path, "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            res = subprocess.run(cmd, capture_output=True, text=True)
-            if res.returncode != 0:
-                raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
-            objs.append(obj)
-        tmp_lib = os.path.join(tmp, "libw4a8.so")
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+def _link(cc, tmp, sources, out, verbose, debug):
+    objs = []
+    for src in sources:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(tmp, src.replace(".", "_") + ".o")
+        cmd = [cc, "-x", "hip", *compile_flags(debug), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
-            raise RuntimeError(f"link failed:\n{res.stderr}")
-        shutil.copyfile(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
+        objs.append(obj)
+    tmp_lib = os.path.join(tmp, os.path.basename(out))
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    shutil.copyfile(tmp_lib, out + ".tmp")
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source, check the device assembly of the inline-asm
+    kernels, and link libw4a8.so and libw4a8_probe.so; returns the GEMM
+    library's path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="w4a8_build_") as tmp:
+        if not debug:
+            check_device_asm(cc, tmp, verbose)
+        _link(cc, tmp, SOURCES, LIB, verbose, debug)
+        _link(cc, tmp, PROBE_SOURCES, PROBE_LIB, verbose, debug)
     return LIB
 
 

@@ -105,3 +105,23 @@ def test_binding_fails_loudly_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(RuntimeError):
         w4a8.load(require_device=True)
+
+
+def test_probe_library_exports_and_host_checks():
+    path = os.path.join(ROOT, "moe_grouped_precision_amd", "libw4a8_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    probe = ctypes.CDLL(path)
+    for name in ("w4a8_probe_mfma", "w4a8_probe_read"):
+        assert hasattr(probe, name)
+    probe.w4a8_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    probe.w4a8_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    # argument errors are reported before anything is launched
+    assert probe.w4a8_probe_mfma(4, 0, 16, 8, None, None) == 1
+    assert probe.w4a8_probe_mfma(4, 0, 0, 8, P16, None) == 2
+    assert probe.w4a8_probe_mfma(1, 2, 16, 8, P16, None) == 2
+    assert probe.w4a8_probe_read(None, 1024, 8, P16, None) == 1
+    assert probe.w4a8_probe_read(P16, 1000, 8, P16, None) == 2
+    assert probe.w4a8_probe_read(P4, 1024, 8, P16, None) == 4
