@@ -37,7 +37,8 @@ DEFAULT_STEPS = {"prefill_gateup": 20}
 BOUND = {"prefill_gateup": "mfma", "prefill_down": "mfma"}
 
 
-KERNEL_SOURCES = ("moe_grouped_precision_amd/csrc/gemm.hip", "moe_grouped_precision_amd/csrc/w4a8_device.h")
+KERNEL_SOURCES = tuple("moe_grouped_precision_amd/csrc/" + f for f in (
+    "gemm.hip", "stream_phase.h", "mfma_phase.h", "w4a8_kernel.h", "w4a8_device.h"))
 
 
 def log(msg):

@@ -33,7 +33,7 @@ struct DeviceInfo {
   bool ready = false;
   bool supported = false;
   int cus = 0;
-  int grid = 0;
+  int grid = 0;  // workgroups of the persistent GEMM launch (one per CU)
 };
 
 constexpr int kMaxDevices = 64;
@@ -56,7 +56,7 @@ int device_info(const DeviceInfo** out) {
     d.cus = prop.multiProcessorCount;
     if (d.supported) {
       int blocks = 0;
-      e = w4a8::occupancy_blocks_per_cu(&blocks);
+      e = w4a8::grouped_gemm_occupancy(&blocks);
       if (e != hipSuccess) return fail(W4A8_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
       d.grid = d.cus * (blocks > 0 ? blocks : 1);
     }

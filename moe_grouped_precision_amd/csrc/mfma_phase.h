@@ -1,0 +1,345 @@
+// MFMA-tile phase of the grouped W4A8 GEMM kernel (gemm.hip): the experts
+// with more than S_MAX rows, whose m-tiles (at most T_MAX rows each, sized
+// per expert by the tile rule) make the contraction compute-bound.  All
+// vector-memory ops of the K loop are inline asm with explicit waits
+// (w4a8_kernel.h); all loads use clamped addresses (padding rows and columns
+// re-read a real one and are never stored).  gfx950 only.
+#pragma once
+
+#include "w4a8_kernel.h"
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------------------
+// Tiles of 512 (n) x 128 (m) per workgroup.
+//
+// Wave w owns columns 64w .. 64w+63 of the tile and all of its rows (4 x 8
+// MFMA blocks, 128 fp32 accumulators per lane).  Every weight byte of the
+// tile is needed by exactly one wave, so weights go from global memory
+// straight into that wave's MFMA operand registers (two register slots: the
+// next group's weights load while the current group's are in use); only the
+// activation rows and the scales, which every wave needs, are staged in LDS
+// through direct global->LDS loads:
+//   X ring   : P2_NX slots x [128 rows][128 B]  (row chunk c at c ^ xkey(row))
+//   SB chunk : 2 x [512 cols][SC] u32  (E8M0 codes of groups SC*c .. SC*c+3,
+//              word gg of column n at gg ^ skey(n))
+//   SA chunk : 2 x [128 rows][SC] fp32 (word gg of row r at gg ^ skey(r))
+// Stage s (one K group): wait until the weights of group s (and everything
+// issued before them) have landed, barrier, issue the weights of group s + 1,
+// the scale chunk that group s + 2 opens (if any) and the activation rows of
+// group s + 2, then the 32 MFMAs of the group.  One in-order counter per wave
+// sets the depths: waiting for the weights of group s also waits for
+// everything issued before them, so the activation rows, issued last, run one
+// stage further ahead.
+// Per 128-K group a workgroup reads 32 KB of weights and 16 KB of activations
+// for 256 MFMAs, the fewest bytes per MFMA of the tile shapes whose
+// accumulators fit two waves per SIMD.
+// ---------------------------------------------------------------------------
+constexpr int MF_THREADS = 512;
+constexpr int MF_WAVES = MF_THREADS / 64;
+constexpr int MF_BN = TN_MFMA;          // 512 weight columns
+constexpr int MF_BM = T_MAX;            // 128 activation rows
+constexpr int P2_DX = 2;                // activation groups ahead (weights: one)
+constexpr int P2_NX = P2_DX + 1;        // activation ring slots
+constexpr int P2_XSLOT = MF_BM * 128;   // 16 KB
+constexpr int P2_SB = P2_NX * P2_XSLOT;
+constexpr int P2_SBBUF = MF_BN * SC * 4;  // 8 KB
+constexpr int P2_SA = P2_SB + 2 * P2_SBBUF;
+constexpr int P2_SABUF = MF_BM * SC * 4;  // 2 KB
+constexpr int P2_BYTES = P2_SA + 2 * P2_SABUF;
+constexpr int P2_X_OPS = MF_BM * 128 / 1024 / MF_WAVES;  // activation loads per wave per stage
+static_assert(MF_BN == 64 * MF_WAVES, "each wave owns 64 columns");
+static_assert(P2_X_OPS * 1024 * MF_WAVES == MF_BM * 128, "activation loads cover the slot");
+static_assert(MF_BN * SC == MF_WAVES * 4 * 64, "four 4-byte E8M0 loads per lane cover a chunk");
+static_assert(MF_BM * SC == MF_WAVES * 64, "one 4-byte activation-scale load per lane covers a chunk");
+// a scale buffer is refilled P2_DX stages ahead, after every stage of the
+// chunk two back has passed the barrier of the stage that refills it
+static_assert(P2_DX <= SC, "scale chunk reuse distance");
+
+// LDS addresses of this lane's fragments in a stage slot / scale buffer: row
+// block mi adds the immediate mi * 2048 (X) or mi * 256 (SA).  Row m = 16 mi
+// + i has activation key xkey(m) = xkey(i) for every mi, and scale key
+// skey<SC>(m) = ((2 mi) & 3) ^ (i >> 3): one scale address for even mi, one
+// for odd.
+struct P2Lds {
+  const uint8_t* x0;   // chunk q of row i
+  const uint8_t* x1;   // chunk q + 4 of row i
+  const uint8_t* sa0;  // scale (row i, group gg), even mi
+  const uint8_t* sa1;  // odd mi
+};
+
+__device__ __forceinline__ void p2_read_x(const P2Lds& a, int mi, v4i& x0, v4i& x1, float& sa) {
+  x0 = lds128(a.x0 + mi * 2048);
+  x1 = lds128(a.x1 + mi * 2048);
+  sa = ldsf(((mi & 1) ? a.sa1 : a.sa0) + mi * 16 * SC * 4);
+}
+
+template <int NMB>
+struct MfmaTile {
+  const GemmArgs& p;
+  uint8_t* lds;
+  int e, row0, rows, n0, R, G, wn, q, r16, xl0, xl1;
+  bool wvalid;
+  const uint8_t* xt;
+  const uint8_t* wt;
+  uint32_t xo[P2_X_OPS];
+  uint32_t wo[4];
+
+  __device__ __forceinline__ MfmaTile(const GemmArgs& p_, uint8_t* lds_, int e_, int row0_, int rows_,
+                                      int n0_, int R_)
+      : p(p_), lds(lds_), e(e_), row0(row0_), rows(rows_), n0(n0_), R(R_) {
+    // opaque lane: the per-lane constants below are computed per tile, not
+    // hoisted out of the tile loop where they would be live across it
+    const int lane = opaque_lane(), wave = threadIdx.x >> 6;
+    const int K = p.K, N = p.N;
+    G = K >> 7;
+    wn = wave;
+    q = lane >> 4;
+    r16 = lane & 15;
+    wvalid = uniform(n0 + wn * 64) < N;  // wave has columns inside N
+    // tile bases (uniform) and per-lane 32-bit offsets: K <= 2^20 keeps every
+    // in-tile offset below 2^32
+    xt = p.A + (size_t)row0 * K;
+    wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
+#pragma unroll
+    for (int i = 0; i < P2_X_OPS; ++i) {
+      const int r = (wave * P2_X_OPS + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ xkey(r);
+      xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = min(n0 + wn * 64 + nb * 16 + r16, N - 1);
+      wo[nb] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
+    }
+    // LDS byte offsets of this lane's activation fragments within a slot
+    xl0 = r16 * 128 + ((q ^ xkey(r16)) << 4);
+    xl1 = r16 * 128 + (((q + 4) ^ xkey(r16)) << 4);
+  }
+
+  // One weight load of group g: 16 columns (block nb) x 64 B into w.
+  __device__ __forceinline__ void load_w(v4i& w, int nb, int g) const {
+    vm_load16(w, wt + (size_t)max(0, min(g, G - 1)) * 64, wo[nb], live_mask(g >= 0 && g < G));
+  }
+
+  // One activation load of group g: 8 rows x 128 B into ring slot g % P2_NX.
+  __device__ __forceinline__ void load_x(int i, int g) const {
+    const int wave = uniform(threadIdx.x >> 6);
+    vm_dma16(xt + (size_t)min(g, G - 1) * 128, xo[i],
+             lds_u32(lds + (g % P2_NX) * P2_XSLOT + (wave * P2_X_OPS + i) * 1024), live_mask(g < G));
+  }
+
+  // Scale chunk c: 512 columns x SC groups of E8M0 words (four 4-byte loads
+  // per wave) and 128 rows x SC groups of activation scales (one per wave).
+  // Four lanes read one column's (row's) 16 contiguous bytes; word gg of a
+  // column (row) r lands at position gg ^ skey(r).  (One 16-byte load per
+  // lane instead, four times fewer instructions, measured slower.)
+  __device__ __forceinline__ void load_scales(int c) const {
+    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
+    const int K = p.K, N = p.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // rows [col] of SC words
+      const int g = min(SC * c + ((lane & 3) ^ skey<SC>(col)), G - 1);
+      const int n = min(n0 + col, N - 1);
+      vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+              lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
+    }
+    const int r = (wave * 64 + lane) >> 2;  // rows [row] of SC words
+    const int g = min(SC * c + ((lane & 3) ^ skey<SC>(r)), G - 1);
+    const size_t row = (size_t)row0 + min(r, rows - 1);
+    vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P2_SA + (c & 1) * P2_SABUF + wave * 256));
+  }
+
+  // The loads issued at stage s, in issue order: the weights of group s + 1,
+  // the scale chunk that group s + 2 opens (if any), the activation rows of
+  // group s + 2.  Stages past the last group issue them with no lanes, so every
+  // stage issues the same loads and every wait is one constant.
+  __device__ __forceinline__ void issue(int s, v4i (&wnext)[4]) const {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) load_w(wnext[nb], nb, s + 1);
+    if (s + 2 < G && (s + 2) % SC == 0) load_scales((s + 2) / SC);
+#pragma unroll
+    for (int i = 0; i < P2_X_OPS; ++i) load_x(i, s + 2);
+  }
+
+  // One K group: step mi issues the LDS reads of block mi+1, the four MFMAs
+  // of block mi and the promotion of the previous step's partials (carried
+  // across stages in prev/sprev, so the first step of a stage has arithmetic
+  // to do while its reads are in flight); the scheduling fences keep each
+  // step's work together.  (No memory instruction goes between the steps: an
+  // asm statement there lengthens the live ranges of the fragment reads past
+  // the register budget, and the accumulators spill.)
+  __device__ __forceinline__ void group(v4f (&acc)[8][4], v4f (&prev)[4], float& sprev, const v4i (&w)[4],
+                                        const P2Lds& a, const int (&sbv)[4]) const {
+    v4i xa0, xa1;
+    float saa;
+    p2_read_x(a, 0, xa0, xa1, saa);
+#pragma unroll
+    for (int mi = 0; mi < NMB; ++mi) {
+      v4i xb0 = xa0, xb1 = xa1;
+      float sab_n = saa;
+      if (mi + 1 < NMB) p2_read_x(a, mi + 1, xb0, xb1, sab_n);
+      // the previous step's block: the last block of the previous group when mi == 0
+      const int pm = mi == 0 ? NMB - 1 : mi - 1;
+      v4f pn[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) pn[nb] = mfma_group(w[nb], xa0, xa1, sbv[nb]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) promote(acc[pm][nb], sprev, prev[nb]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) prev[nb] = pn[nb];
+      sprev = saa;
+      xa0 = xb0;
+      xa1 = xb1;
+      saa = sab_n;
+      // step order: the next block's LDS reads, then each MFMA followed by four
+      // of the promotions, which run while the matrix core works
+      if (mi + 1 < NMB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Stage s: the weights of group s and everything issued before them have
+  // landed once at most the P2_X_OPS newest loads (the activation rows of
+  // group s + 1) are in flight
+  __device__ __forceinline__ void stage(int s, v4i (&wcur)[4], v4i (&wnext)[4], v4f (&acc)[8][4],
+                                        v4f (&prev)[4], float& sprev) {
+    wait_vm<P2_X_OPS>();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) tie(wcur[nb]);
+    wg_barrier();
+    issue(s, wnext);
+    const uint8_t* slot = lds + (s % P2_NX) * P2_XSLOT;
+    const uint8_t* sbb = lds + P2_SB + ((s / SC) & 1) * P2_SBBUF;
+    const uint8_t* sab = lds + P2_SA + ((s / SC) & 1) * P2_SABUF;
+    const int gg = s % SC;
+    // column wn*64 + 16 nb + r16 (and row r16 + 16 mi) has scale key
+    // ((2 nb) & 3) ^ (r16 >> 3) (((2 mi) & 3) ^ (r16 >> 3))
+    const int k0 = gg ^ (r16 >> 3);
+    const uint8_t* sbl0 = sbb + ((wn * 64 + r16) * SC + k0) * 4;
+    const uint8_t* sbl1 = sbb + ((wn * 64 + r16) * SC + (k0 ^ 2)) * 4;
+    int sbv[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      sbv[nb] = (int)((lds32(((nb & 1) ? sbl1 : sbl0) + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
+    P2Lds a;
+    a.x0 = slot + xl0;
+    a.x1 = slot + xl1;
+    a.sa0 = sab + (r16 * SC + k0) * 4;
+    a.sa1 = sab + (r16 * SC + (k0 ^ 2)) * 4;
+    if (wvalid) group(acc, prev, sprev, wcur, a, sbv);
+  }
+
+  __device__ __forceinline__ void run() {
+    // zero accumulators, made opaque so that the compiler does not peel the
+    // first K group to specialise it for zero inputs (a second copy of the
+    // loop body with its own register assignment)
+    v4f acc[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+v"(acc[a][b]));
+      }
+    v4f prev[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      prev[b] = v4f{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+v"(prev[b]));
+    }
+    float sprev = 0.f;
+    asm volatile("" : "+v"(sprev));
+    v4i w0[4], w1[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) w0[nb] = w1[nb] = v4i{0, 0, 0, 0};
+
+    // prologue: the loads of stages -2 and -1 (weights of group 0 land in w0;
+    // the weights "of group -1" are issued with no lanes, to keep the counts
+    // of every stage equal)
+    issue(-2, w1);
+    issue(-1, w0);
+    // whole pairs of stages, then the last odd one: no control-flow path
+    // skips a stage and then runs a later one
+    int s = 0;
+    for (; s + 2 <= G; s += 2) {
+      stage(s, w0, w1, acc, prev, sprev);
+      stage(s + 1, w1, w0, acc, prev, sprev);
+    }
+    if (s < G) stage(s, w0, w1, acc, prev, sprev);
+    wait_vm<0>();  // every load has retired; the ties keep their registers reserved until here
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      tie(w0[nb]);
+      tie(w1[nb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) promote(acc[NMB - 1][nb], sprev, prev[nb]);
+    __syncthreads();  // every wave is done with the ring before the next tile's loads
+
+    if (wvalid) {
+      // lane coordinates recomputed (opaque) rather than kept live through the K loop
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+      const int eq = (t >> 4) & 3, er = t & 15;
+      const int ncol = n0 + (t >> 6) * 64 + eq * 4;
+      const int N = p.N;
+#pragma unroll
+      for (int mi = 0; mi < NMB; ++mi) {
+        const int m = mi * 16 + er;
+        if (m < rows) {
+          uint16_t* crow = p.C + (size_t)(row0 + m) * N;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int n = ncol + nb * 16;
+            if (n < N) store_bf16x4(crow + n, acc[mi][nb]);
+          }
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void mfma_tile(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
+                                          int n0, int R) {
+  switch ((rows + 15) >> 4) {
+    case 1: MfmaTile<1>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 2: MfmaTile<2>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 3: MfmaTile<3>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 4: MfmaTile<4>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 5: MfmaTile<5>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 6: MfmaTile<6>(p, lds, e, row0, rows, n0, R).run(); break;
+    case 7: MfmaTile<7>(p, lds, e, row0, rows, n0, R).run(); break;
+    default: MfmaTile<8>(p, lds, e, row0, rows, n0, R).run(); break;
+  }
+}
+
+// Work item of round r for workgroup b.  Workgroups are dealt to the eight
+// XCDs round-robin (b % 8), each XCD with its own L2, so the items of one
+// round are regrouped to give every XCD a contiguous block of item numbers.
+__device__ __forceinline__ int xcd_item(int r, int b, int grid) {
+  if ((grid & 7) != 0) return r * grid + b;
+  return r * grid + (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+// Item number -> (m-tile, n-tile): bands of P2_SUPER m-tiles, n-tiles in
+// order within a band and m fastest, so a block of consecutive items shares
+// a few m-tiles (activation rows) and a few n-tiles (weight columns): the 32
+// items an XCD runs at once cover 8 m-tiles x 4 n-tiles, whose 128 KB of
+// activations and 128 KB of weights per K group are what its L2 fetches.
+constexpr int P2_SUPER = 8;
+__device__ __forceinline__ void item_tile(int L, int MT, int NT, int* mt, int* nt) {
+  const int band = L / (P2_SUPER * NT);
+  const int rem = L - band * P2_SUPER * NT;
+  const int rg = min(P2_SUPER, MT - band * P2_SUPER);
+  *mt = band * P2_SUPER + rem % rg;
+  *nt = rem / rg;
+}
+
+}  // namespace w4a8

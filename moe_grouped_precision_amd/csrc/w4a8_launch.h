@@ -22,6 +22,6 @@ hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts, 
 hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int max_tiles,
                        hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream);
-hipError_t occupancy_blocks_per_cu(int* blocks);
+hipError_t grouped_gemm_occupancy(int* blocks);
 
 }  // namespace w4a8
