@@ -27,27 +27,54 @@ grouped_gemm_kernel(GemmArgs p) {
   __shared__ int s_off[MAX_EXPERTS + 1];
   __shared__ int s_sbase[MAX_EXPERTS + 1];
   __shared__ int s_mbase[MAX_EXPERTS + 1];
-  __shared__ int s_info[2];
+  __shared__ int s_info[3];
   if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info)) return;
   const int R = uniform(s_off[p.E]);
 
-  // phase 1: streaming items, one workgroup each
+  // phase 1: streaming items
   {
     const int tiles = uniform(s_sbase[p.E]);
-    const int nbw = stream_width_blocks(tiles, p.N, gridDim.x);
-    const int width = 64 * nbw;
-    const int nchunks = (p.N + width - 1) / width;
-    const long long items = (long long)tiles * nchunks;
-    for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-      const int mt = (int)(it / nchunks);
-      const int n0 = (int)(it % nchunks) * width;
-      const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
-      const int row0 = uniform(s_off[e]);
-      const int rows = uniform(s_off[e + 1]) - row0;
-      switch (nbw) {
-        case 1: stream_item<1>(p, lds, e, row0, rows, n0, R); break;
-        case 2: stream_item<2>(p, lds, e, row0, rows, n0, R); break;
-        default: stream_item<3>(p, lds, e, row0, rows, n0, R); break;
+    const int nu = (p.N + 63) / 64;
+    if (tiles > 0 && uniform(s_info[1]) == uniform(s_info[2]) &&
+        (long long)tiles * nu >= 2LL * gridDim.x) {
+      // every streaming tile has the same row blocks, so every 64-column unit
+      // costs the same: an equal share of units per workgroup (with fewer
+      // than two units per workgroup, dealing whole items measured faster)
+      long long u = 0, u_end = 0;
+      stream_range(tiles, nu, blockIdx.x, gridDim.x, &u, &u_end);
+      while (u < u_end) {
+        const int mt = (int)(u / nu);
+        const int c0 = (int)(u - (long long)mt * nu);
+        const int w = (int)min((long long)min(P1_MAXNBW, nu - c0), u_end - u);
+        const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
+        const int row0 = uniform(s_off[e]);
+        const int rows = uniform(s_off[e + 1]) - row0;
+        switch (w) {
+          case 1: stream_item<1>(p, lds, e, row0, rows, c0 * 64, R); break;
+          case 2: stream_item<2>(p, lds, e, row0, rows, c0 * 64, R); break;
+          default: stream_item<3>(p, lds, e, row0, rows, c0 * 64, R); break;
+        }
+        u += w;
+      }
+    } else {
+      // tiles of different row counts cost different amounts per column:
+      // items of one width dealt round-robin, so a workgroup's items come from
+      // several experts
+      const int nbw = stream_width_blocks(tiles, p.N, gridDim.x);
+      const int width = 64 * nbw;
+      const int nchunks = (p.N + width - 1) / width;
+      const long long items = (long long)tiles * nchunks;
+      for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+        const int mt = (int)(it / nchunks);
+        const int n0 = (int)(it % nchunks) * width;
+        const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
+        const int row0 = uniform(s_off[e]);
+        const int rows = uniform(s_off[e + 1]) - row0;
+        switch (nbw) {
+          case 1: stream_item<1>(p, lds, e, row0, rows, n0, R); break;
+          case 2: stream_item<2>(p, lds, e, row0, rows, n0, R); break;
+          default: stream_item<3>(p, lds, e, row0, rows, n0, R); break;
+        }
       }
     }
   }

@@ -314,10 +314,11 @@ __device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int
   }
 }
 
-// Item width for the streaming phase: the width (64*NBW columns) that
-// minimises rounds x per-item bytes, per-item bytes ~ weights (32*NBW per K)
-// plus activation rows (about 32 per K).  Wider items re-read the activation
-// rows less often; narrower items spread few experts over more workgroups.
+// Item width for the streaming phase, when items are dealt round-robin: the
+// width (64*NBW columns) that minimises rounds x per-item bytes, per-item
+// bytes ~ weights (32*NBW per K) plus activation rows (about 32 per K).  Wider
+// items re-read the activation rows less often; narrower items spread few
+// experts over more workgroups.
 __device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
   int best = 1;
   long long best_cost = -1;
@@ -331,6 +332,34 @@ __device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
     }
   }
   return best;
+}
+
+// Work split of the streaming phase when every streaming tile has the same
+// row blocks and there are at least two units per workgroup: the contiguous
+// range [*u0, *u1) of the
+// U = tiles * nu units of 64 columns (unit u = column block u % nu of
+// streaming m-tile u / nu) that workgroup b of `grid` streams.  Every expert
+// tile's units cost the same weight bytes whatever its rows, so
+//   tiles < grid:  tile t gets workgroups [t*grid/tiles, (t+1)*grid/tiles)
+//                  (21 or 22 each at 12 tiles on 256 CUs) and splits its nu
+//                  units evenly among them: no range spans two experts;
+//   tiles >= grid: workgroup b gets units [U*b/grid, U*(b+1)/grid).
+// A range is run as items of at most P1_MAXNBW units that never span two
+// experts.  Against dealing fixed 192-column items round-robin this lowers
+// the largest share (E=12, 64 routed rows, N=6144: 5 units instead of 6).
+__device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid, long long* u0, long long* u1) {
+  if (tiles < grid) {
+    const int t = (int)(((long long)(b + 1) * tiles - 1) / grid);
+    const int s0 = (int)((long long)t * grid / tiles);
+    const int k = (int)((long long)(t + 1) * grid / tiles) - s0;  // >= 1 since grid > tiles
+    const int j = b - s0;
+    *u0 = (long long)t * nu + (long long)j * nu / k;
+    *u1 = (long long)t * nu + (long long)(j + 1) * nu / k;
+  } else {
+    const long long U = (long long)tiles * nu;
+    *u0 = U * b / grid;
+    *u1 = U * (b + 1) / grid;
+  }
 }
 
 }  // namespace w4a8

@@ -138,6 +138,7 @@ __device__ inline int wave_max_nonneg(int x) {
 //   s_mbase[0..E]  first MFMA-class m-tile of each expert;      [E] = total
 //   s_info[0]      nonzero if the offsets are invalid
 //   s_info[1]      row blocks (GRAN rows) of the largest streaming tile
+//   s_info[2]      row blocks of the smallest streaming tile (0 if none)
 // Returns false (uniformly across the block) if the offsets are invalid.
 // ---------------------------------------------------------------------------
 __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int* s_off,
@@ -146,7 +147,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
     const int lane = threadIdx.x;
     const int per = (E + 64) / 64;  // offsets per lane, so that 64 * per > E
     const int i0 = lane * per;
-    int bad = 0, ls = 0, lm = 0, mb = 0;
+    int bad = 0, ls = 0, lm = 0, mb = 0, mbi = 0;  // mbi: S_MAX/GRAN - row blocks
     for (int k = 0; k < per; ++k) {
       const int e = i0 + k;
       if (e <= E) {
@@ -160,6 +161,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
           if (t.cls == CLASS_STREAM) {
             ls += t.n_m;
             mb = max(mb, t.tile_m / GRAN);
+            mbi = max(mbi, S_MAX / GRAN - t.tile_m / GRAN);
           }
           if (t.cls == CLASS_MFMA) lm += t.n_m;
         }
@@ -168,6 +170,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
     const bool any_bad = __ballot(bad != 0) != 0;
     const int is = wave_inclusive_sum(ls), im = wave_inclusive_sum(lm);
     const int mbmax = wave_max_nonneg(mb);
+    const int mbimax = wave_max_nonneg(mbi);
     if (!any_bad) {
       int rs = is - ls, rm = im - lm;
       for (int k = 0; k < per; ++k) {
@@ -186,6 +189,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
       s_mbase[E] = __builtin_amdgcn_readlane(im, 63);
       s_info[0] = any_bad;
       s_info[1] = mbmax;
+      s_info[2] = mbmax > 0 ? S_MAX / GRAN - mbimax : 0;
     }
   }
   __syncthreads();

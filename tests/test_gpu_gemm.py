@@ -144,6 +144,8 @@ def test_layouts_bit_identical_and_deterministic(gpu_lib):
     ([0, 0, 0, 70, 0], 288, 256),     # empty experts around one MFMA expert
     ([64, 65, 16, 17, 48, 49], 320, 384),
     (list(range(0, 140, 7)), 256, 128),
+    ([5] * 300, 192, 128),            # more streaming tiles than CUs, all one row block
+    ([40] * 3 + [0] + [33] * 2, 8192, 256),  # equal row blocks: units split per expert
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
