@@ -29,6 +29,17 @@ extern "C" {
 int w4a8_probe_mfma(int fmt_a, int fmt_b, int iters, int blocks, float* sink_dev, void* stream);
 
 /*
+ * w4a8_probe_mfma_data -- as w4a8_probe_mfma, but each thread's operands are
+ * read from ops_dev: int32 [blocks * 256][16] (words 0-7 the A operand, 8-15
+ * the B operand; for an FP4 operand only its first four words are used).
+ * Filled with random bits it measures the sustained rate on realistic data,
+ * which is well below the rate on constant operands.  Any bit pattern is
+ * allowed (NaN codes only make NaN results).
+ */
+int w4a8_probe_mfma_data(int fmt_a, int fmt_b, int iters, int blocks, const int32_t* ops_dev,
+                         float* sink_dev, void* stream);
+
+/*
  * w4a8_probe_read -- reads `bytes` bytes from buf_dev once (16-byte loads,
  * grid-stride, eight loads in flight per lane) and writes one int to
  * sink_dev.  bytes must be a positive multiple of 16; buf_dev 16-byte aligned.

@@ -163,14 +163,13 @@ struct MfmaTile {
     for (int i = 0; i < P2_X_OPS; ++i) load_x(i, s + 2);
   }
 
-  // One K group: step mi issues the LDS reads of block mi+1, the four MFMAs
-  // of block mi and the promotion of the previous step's partials (carried
-  // across stages in prev/sprev, so the first step of a stage has arithmetic
-  // to do while its reads are in flight); the scheduling fences keep each
-  // step's work together.  (No memory instruction goes between the steps: an
-  // asm statement there lengthens the live ranges of the fragment reads past
-  // the register budget, and the accumulators spill.)
-  __device__ __forceinline__ void group(v4f (&acc)[8][4], v4f (&prev)[4], float& sprev, const v4i (&w)[4],
+  // One K group: step mi issues the LDS reads of block mi+1 and the four
+  // MFMAs of block mi; after each MFMA come the four promotion FMAs of the
+  // partial two MFMAs back (the last two partials of a group are carried into
+  // the next group in pq, with their row block's scale in sprev), so the
+  // FMAs never wait for the MFMA just issued and only three partials are
+  // live at a time.  The scheduling fences keep each step's work together.
+  __device__ __forceinline__ void group(v4f (&acc)[8][4], v4f (&pq)[2], float& sprev, const v4i (&w)[4],
                                         const P2Lds& a, const int (&sbv)[4]) const {
     v4i xa0, xa1;
     float saa;
@@ -180,15 +179,17 @@ struct MfmaTile {
       v4i xb0 = xa0, xb1 = xa1;
       float sab_n = saa;
       if (mi + 1 < NMB) p2_read_x(a, mi + 1, xb0, xb1, sab_n);
-      // the previous step's block: the last block of the previous group when mi == 0
+      // the block before this one: the last block of the previous group when mi == 0
       const int pm = mi == 0 ? NMB - 1 : mi - 1;
-      v4f pn[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) pn[nb] = mfma_group(w[nb], xa0, xa1, sbv[nb]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) promote(acc[pm][nb], sprev, prev[nb]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) prev[nb] = pn[nb];
+      for (int nb = 0; nb < 4; ++nb) {
+        const v4f r = mfma_group(w[nb], xa0, xa1, sbv[nb]);
+        if (nb >= 2)
+          promote(acc[mi][nb - 2], saa, pq[nb & 1]);
+        else
+          promote(acc[pm][nb + 2], sprev, pq[nb & 1]);
+        pq[nb & 1] = r;
+      }
       sprev = saa;
       xa0 = xb0;
       xa1 = xb1;
@@ -209,7 +210,7 @@ struct MfmaTile {
   // landed once at most the P2_X_OPS newest loads (the activation rows of
   // group s + 1) are in flight
   __device__ __forceinline__ void stage(int s, v4i (&wcur)[4], v4i (&wnext)[4], v4f (&acc)[8][4],
-                                        v4f (&prev)[4], float& sprev) {
+                                        v4f (&pq)[2], float& sprev) {
     wait_vm<P2_X_OPS>();
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) tie(wcur[nb]);
@@ -233,7 +234,7 @@ struct MfmaTile {
     a.x1 = slot + xl1;
     a.sa0 = sab + (r16 * SC + k0) * 4;
     a.sa1 = sab + (r16 * SC + (k0 ^ 2)) * 4;
-    if (wvalid) group(acc, prev, sprev, wcur, a, sbv);
+    if (wvalid) group(acc, pq, sprev, wcur, a, sbv);
   }
 
   __device__ __forceinline__ void run() {
@@ -248,11 +249,11 @@ struct MfmaTile {
         acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
         asm volatile("" : "+v"(acc[a][b]));
       }
-    v4f prev[4];
+    v4f pq[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      prev[b] = v4f{0.f, 0.f, 0.f, 0.f};
-      asm volatile("" : "+v"(prev[b]));
+    for (int b = 0; b < 2; ++b) {
+      pq[b] = v4f{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+v"(pq[b]));
     }
     float sprev = 0.f;
     asm volatile("" : "+v"(sprev));
@@ -269,18 +270,18 @@ struct MfmaTile {
     // skips a stage and then runs a later one
     int s = 0;
     for (; s + 2 <= G; s += 2) {
-      stage(s, w0, w1, acc, prev, sprev);
-      stage(s + 1, w1, w0, acc, prev, sprev);
+      stage(s, w0, w1, acc, pq, sprev);
+      stage(s + 1, w1, w0, acc, pq, sprev);
     }
-    if (s < G) stage(s, w0, w1, acc, prev, sprev);
+    if (s < G) stage(s, w0, w1, acc, pq, sprev);
     wait_vm<0>();  // every load has retired; the ties keep their registers reserved until here
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       tie(w0[nb]);
       tie(w1[nb]);
     }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) promote(acc[NMB - 1][nb], sprev, prev[nb]);
+    promote(acc[NMB - 1][2], sprev, pq[0]);
+    promote(acc[NMB - 1][3], sprev, pq[1]);
     __syncthreads();  // every wave is done with the ring before the next tile's loads
 
     if (wvalid) {

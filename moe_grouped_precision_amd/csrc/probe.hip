@@ -36,6 +36,33 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float* sink)
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The same MFMA stream with operands loaded per lane from `ops` (16 words per
+// thread: 8 for the A operand, 8 for B), so that they can be random bits
+// rather than constants: the matrix core's sustained rate depends on the
+// operand data (all-equal operands run about twice as fast as random ones).
+template <int FA, int FB>
+__global__ void __launch_bounds__(256) mfma_probe_data_kernel(int iters, const int* __restrict__ ops, float* sink) {
+  const int* o = ops + ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  v8i a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = o[k];
+    b[k] = o[8 + k];
+  }
+  v4f acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[k], FA, FB, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+  sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 __global__ void __launch_bounds__(256) read_probe_kernel(const v4i* __restrict__ p, size_t n16, int* sink) {
   constexpr int U = 8;
   v4i acc = {0, 0, 0, 0};
@@ -76,5 +103,21 @@ extern "C" int w4a8_probe_read(const void* buf_dev, size_t bytes, int blocks, in
   if (reinterpret_cast<uintptr_t>(buf_dev) % 16) return W4A8_ERR_ALIGN;
   hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const v4i*>(buf_dev), bytes / 16, sink_dev);
+  return hipGetLastError() == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+extern "C" int w4a8_probe_mfma_data(int fmt_a, int fmt_b, int iters, int blocks, const int32_t* ops_dev,
+                                    float* sink_dev, void* stream) {
+  if (!sink_dev || !ops_dev) return W4A8_ERR_NULL;
+  if (iters <= 0 || blocks <= 0) return W4A8_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt_a == 4 && fmt_b == 0)
+    hipLaunchKernelGGL((mfma_probe_data_kernel<4, 0>), dim3(blocks), dim3(256), 0, s, iters, ops_dev, sink_dev);
+  else if (fmt_a == 0 && fmt_b == 0)
+    hipLaunchKernelGGL((mfma_probe_data_kernel<0, 0>), dim3(blocks), dim3(256), 0, s, iters, ops_dev, sink_dev);
+  else if (fmt_a == 4 && fmt_b == 4)
+    hipLaunchKernelGGL((mfma_probe_data_kernel<4, 4>), dim3(blocks), dim3(256), 0, s, iters, ops_dev, sink_dev);
+  else
+    return W4A8_ERR_SHAPE;
   return hipGetLastError() == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }

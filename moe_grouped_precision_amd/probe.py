@@ -24,6 +24,9 @@ def load():
         lib.w4a8_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p]
         lib.w4a8_probe_mfma.restype = ctypes.c_int
+        lib.w4a8_probe_mfma_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.w4a8_probe_mfma_data.restype = ctypes.c_int
         lib.w4a8_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p]
         lib.w4a8_probe_read.restype = ctypes.c_int
@@ -60,6 +63,28 @@ def mfma_tflops(fmt_a: int, fmt_b: int, iters: int = 4096, reps: int = 5) -> flo
         st = lib.w4a8_probe_mfma(fmt_a, fmt_b, iters, blocks, ctypes.c_void_p(sink.data_ptr()), stream)
         if st != 0:
             raise RuntimeError(f"w4a8_probe_mfma status {st}")
+
+    ms = _time(run, reps)
+    flops = blocks * 4 * iters * 8 * MFMA_FLOPS
+    return flops / (ms * 1e-3) / 1e12
+
+
+def mfma_tflops_random(fmt_a: int, fmt_b: int, iters: int = 4096, reps: int = 5, seed: int = 0) -> float:
+    """Sustained TFLOP/s of the same MFMA stream on random operand bits (one
+    set per thread, fixed over the loop), eight waves per SIMD."""
+    lib = load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cus * 8
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    ops = torch.randint(-2**31, 2**31 - 1, (blocks * 256 * 16,), dtype=torch.int32, device="cuda", generator=g)
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        st = lib.w4a8_probe_mfma_data(fmt_a, fmt_b, iters, blocks, ctypes.c_void_p(ops.data_ptr()),
+                                      ctypes.c_void_p(sink.data_ptr()), stream)
+        if st != 0:
+            raise RuntimeError(f"w4a8_probe_mfma_data status {st}")
 
     ms = _time(run, reps)
     flops = blocks * 4 * iters * 8 * MFMA_FLOPS

@@ -112,7 +112,7 @@ def test_probe_library_exports_and_host_checks():
     if not os.path.exists(path):
         pytest.skip("probe library not built")
     probe = ctypes.CDLL(path)
-    for name in ("w4a8_probe_mfma", "w4a8_probe_read"):
+    for name in ("w4a8_probe_mfma", "w4a8_probe_mfma_data", "w4a8_probe_read"):
         assert hasattr(probe, name)
     probe.w4a8_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
@@ -122,6 +122,10 @@ def test_probe_library_exports_and_host_checks():
     assert probe.w4a8_probe_mfma(4, 0, 16, 8, None, None) == 1
     assert probe.w4a8_probe_mfma(4, 0, 0, 8, P16, None) == 2
     assert probe.w4a8_probe_mfma(1, 2, 16, 8, P16, None) == 2
+    probe.w4a8_probe_mfma_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.w4a8_probe_mfma_data(4, 0, 16, 8, None, P16, None) == 1
+    assert probe.w4a8_probe_mfma_data(4, 0, 0, 8, P16, P16, None) == 2
     assert probe.w4a8_probe_read(None, 1024, 8, P16, None) == 1
     assert probe.w4a8_probe_read(P16, 1000, 8, P16, None) == 2
     assert probe.w4a8_probe_read(P4, 1024, 8, P16, None) == 4
