@@ -15,64 +15,91 @@
 
 namespace w4a8 {
 
-// One workgroup of W waves.  Dynamic LDS: hist[W*E] + s_tot[E] + s_wave[16].
+// B workgroups of W waves; workgroup b owns the contiguous slots
+// [b*chunk, (b+1)*chunk) and writes their rows.  Every workgroup histograms
+// all n ids (the slots before its chunk, its own chunk per wave, the slots
+// after it), so it knows each expert's offset and how many of the expert's
+// slots precede its chunk without any exchange between workgroups; workgroup
+// 0 also writes counts and offsets.  Reading all ids in every workgroup costs
+// L2 bandwidth only (the ids of a 16384-token batch are 512 KB), and the
+// result does not depend on the number of workgroups.
+// Dynamic LDS: own[W*E] + bef[W*E] + aft[W*E] + s_tot[E] + s_wave[16].
 __global__ void __launch_bounds__(1024)
-route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits,
+route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int chunk,
                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                   int32_t* __restrict__ row_of_slot) {
   extern __shared__ int smem[];
   const int W = blockDim.x >> 6;
-  int* hist = smem;               // [W][E]: counts, then running row per (wave, expert)
-  int* s_tot = smem + W * E;      // [E]
+  int* own = smem;                // [W][E]: chunk counts per wave, then running row per (wave, expert)
+  int* bef = smem + W * E;        // [W][E]: ids before the chunk
+  int* aft = bef + W * E;         // [W][E]: ids after the chunk
+  int* s_tot = aft + W * E;       // [E]
   int* s_wave = s_tot + E;        // [16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  for (int i = tid; i < W * E; i += blockDim.x) hist[i] = 0;
+  for (int i = tid; i < 3 * W * E; i += blockDim.x) smem[i] = 0;
   __syncthreads();
 
-  // each wave owns one contiguous span of flat slots, a multiple of 64 long
-  const int span = (((n + W - 1) / W) + 63) & ~63;
-  const int begin = min(n, wave * span);
-  const int end = min(n, begin + span);
+  const int cbegin = min(n, (int)blockIdx.x * chunk);
+  const int cend = min(n, cbegin + chunk);
+  // each wave owns one contiguous span of the chunk, a multiple of 64 long
+  const int span = (((cend - cbegin + W - 1) / W) + 63) & ~63;
+  const int begin = min(cend, cbegin + wave * span);
+  const int end = min(cend, begin + span);
 
-  // phase 1: per-wave histograms (order of the LDS atomics does not matter)
+  // phase 1: histograms (the order of the LDS atomics does not matter)
+  for (int i = tid; i < cbegin; i += blockDim.x) {
+    const int id = ids[i];
+    if (id >= 0 && id < E) atomicAdd(&bef[wave * E + id], 1);
+  }
+  for (int i = cend + tid; i < n; i += blockDim.x) {
+    const int id = ids[i];
+    if (id >= 0 && id < E) atomicAdd(&aft[wave * E + id], 1);
+  }
   for (int i = begin + lane; i < end; i += 64) {
-    int id = ids[i];
-    if (id >= 0 && id < E) atomicAdd(&hist[wave * E + id], 1);
+    const int id = ids[i];
+    if (id >= 0 && id < E) atomicAdd(&own[wave * E + id], 1);
   }
   __syncthreads();
 
-  // phase 2: prefix over waves per expert, totals, exclusive scan over experts
+  // phase 2: per expert the slots before the chunk, the prefix of the chunk's
+  // waves, the total; exclusive scan of the totals over experts
   const int per = (E + blockDim.x - 1) / blockDim.x;
   const int e0 = tid * per;
   int local = 0;
   for (int j = 0; j < per; ++j) {
-    int e = e0 + j;
+    const int e = e0 + j;
     if (e < E) {
-      int run = 0;
+      int before = 0, after = 0;
       for (int w = 0; w < W; ++w) {
-        int c = hist[w * E + e];
-        hist[w * E + e] = run;
+        before += bef[w * E + e];
+        after += aft[w * E + e];
+      }
+      int run = before;
+      for (int w = 0; w < W; ++w) {
+        const int c = own[w * E + e];
+        own[w * E + e] = run;
         run += c;
       }
-      s_tot[e] = run;
-      counts[e] = run;
-      local += run;
+      const int tot = run + after;
+      s_tot[e] = tot;
+      if (blockIdx.x == 0) counts[e] = tot;
+      local += tot;
     }
   }
   int total;
   int ex = block_exclusive_scan(local, s_wave, &total);
   for (int j = 0; j < per; ++j) {
-    int e = e0 + j;
+    const int e = e0 + j;
     if (e < E) {
-      offsets[e] = ex;
-      for (int w = 0; w < W; ++w) hist[w * E + e] += ex;
+      if (blockIdx.x == 0) offsets[e] = ex;
+      for (int w = 0; w < W; ++w) own[w * E + e] += ex;
       ex += s_tot[e];
     }
   }
-  if (tid == 0) offsets[E] = total;
+  if (tid == 0 && blockIdx.x == 0) offsets[E] = total;
   __syncthreads();
 
   // phase 3: stable ranks.  Lanes holding the same expert find each other with
@@ -89,9 +116,9 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits,
       m &= bit ? bb : ~bb;
     }
     int row = -1;
-    if (valid) row = hist[wave * E + id] + __popcll(m & below);
+    if (valid) row = own[wave * E + id] + __popcll(m & below);
     __builtin_amdgcn_wave_barrier();
-    if (valid && lane == 63 - __clzll(m)) hist[wave * E + id] += __popcll(m);
+    if (valid && lane == 63 - __clzll(m)) own[wave * E + id] += __popcll(m);
     __builtin_amdgcn_wave_barrier();
     if (i < end) row_of_slot[i] = row;
   }
@@ -166,13 +193,19 @@ plan_kernel(const int32_t* __restrict__ offsets, int E, int N, int32_t* __restri
 
 hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts,
                              int32_t* offsets, int32_t* row_of_slot, hipStream_t stream) {
-  int W = 8192 / E;
+  // three [W][E] histograms in at most 48 KB of LDS
+  int W = 4096 / E;
   if (W > 16) W = 16;
   if (W < 1) W = 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  size_t lds = (size_t)(W * E + E + 16) * sizeof(int);
-  hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(W * 64), lds, stream, ids, n, E, nbits,
+  // chunks of at least 2048 slots (a multiple of 64), at most 256 workgroups
+  constexpr int kMinChunk = 2048, kMaxBlocks = 256;
+  int chunk = kMinChunk;
+  if ((n + chunk - 1) / chunk > kMaxBlocks) chunk = ((n + kMaxBlocks - 1) / kMaxBlocks + 63) & ~63;
+  const int blocks = n > 0 ? (n + chunk - 1) / chunk : 1;
+  size_t lds = (size_t)(3 * W * E + E + 16) * sizeof(int);
+  hipLaunchKernelGGL(route_prep_kernel, dim3(blocks), dim3(W * 64), lds, stream, ids, n, E, nbits, chunk,
                      counts, offsets, row_of_slot);
   return hipGetLastError();
 }
