@@ -1,5 +1,5 @@
 // Device-side pieces shared by the prep, plan and GEMM kernels of libw4a8:
-// the per-expert tile rule, block-wide scans, bf16 rounding and the plan
+// the per-expert tile rule, block-wide scans, wave scans and the plan
 // prologue that every GEMM workgroup runs.  gfx950 only.
 #pragma once
 
@@ -91,16 +91,6 @@ __device__ inline int block_exclusive_scan(int v, int* wave_tot, int* total) {
   __syncthreads();
   *total = tot;
   return base + x - v;
-}
-
-// ---------------------------------------------------------------------------
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-// ---------------------------------------------------------------------------
-__device__ inline uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
 }
 
 // ---------------------------------------------------------------------------

@@ -30,6 +30,7 @@ namespace w4a8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int SC = 4;                  // groups per scale chunk
 
@@ -140,10 +141,16 @@ __device__ __forceinline__ void promote(v4f& acc, float s, v4f p) {
   acc[3] = fmaf(s, p[3], acc[3]);
 }
 
+// Four fp32 -> bf16, round to nearest even, with gfx950's packed conversion
+// (v_cvt_pk_bf16_f32: two values per instruction; denormals are kept, as
+// the kernels run with fp32 denormals preserved; NaN stays NaN).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v) {
+  const v2bf lo = __builtin_convertvector((v2f){v[0], v[1]}, v2bf);
+  const v2bf hi = __builtin_convertvector((v2f){v[2], v[3]}, v2bf);
   uint2 o;
-  o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-  o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+  o.x = __builtin_bit_cast(uint32_t, lo);
+  o.y = __builtin_bit_cast(uint32_t, hi);
   *reinterpret_cast<uint2*>(dst) = o;
 }
 

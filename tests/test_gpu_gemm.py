@@ -79,7 +79,7 @@ def test_gemm_prefill_gateup_sampled(gpu_lib):
     assert err <= TOL
 
 
-def _codes_case(lib, counts, N, K, seed, layout=0, exact=False, a_fill=None, sa_pow2=False):
+def _codes_case(lib, counts, N, K, seed, layout=0, exact=False, a_fill=None, sa_pow2=False, sa_fill=None):
     A, SA, B, SB, off = synth.random_codes_problem(counts, N, K, seed)
     R = int(off[-1])
     if a_fill is not None:
@@ -87,6 +87,8 @@ def _codes_case(lib, counts, N, K, seed, layout=0, exact=False, a_fill=None, sa_
     if sa_pow2:
         g = torch.Generator().manual_seed(seed + 1)
         SA = torch.exp2(torch.randint(-3, 3, SA.shape, generator=g).float())
+    if sa_fill is not None:
+        SA = sa_fill(SA)
     SA_l = SA if layout == 0 else synth.to_m_major(SA)
     C = _run(lib, A.cuda(), SA_l.cuda(), layout, B.cuda(), SB.cuda(), off.cuda())
     ref = grouped_gemm_bf16(A, SA_l.reshape(-1), layout, B, SB, off)
@@ -129,6 +131,33 @@ def test_one_hot_rows_bit_exact(gpu_lib, layout):
         return out
     _codes_case(gpu_lib, MIXED, 256, 384, 11, layout=layout, exact=True, a_fill=one_hot,
                 sa_pow2=True)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_bf16_rounding_ties_bit_exact(gpu_lib, layout):
+    """One-hot rows of 1.0 times activation scales with at most 21 significant
+    bits: every output is one product, exact in fp32 (E2M1 values have at most
+    two significant bits), so the GPU's bf16 rounding must equal the oracle's
+    round-to-nearest-even of the exact value bit for bit.  A third of the
+    scales sit exactly halfway between two bf16 values (1 + j/256, j odd), so
+    ties must go to even."""
+    def one_hot(A):
+        g = torch.Generator().manual_seed(5)
+        R, K = A.shape
+        out = torch.zeros_like(A)
+        k0 = torch.randint(0, K, (R,), generator=g)
+        out[torch.arange(R), k0] = torch.where(torch.rand(R, generator=g) < 0.5, 0x38, 0xB8).to(torch.uint8)
+        return out
+
+    def sa_fill(SA):
+        g = torch.Generator().manual_seed(6)
+        m = torch.randint(0, 1 << 20, SA.shape, generator=g)
+        ties = (2 * torch.randint(0, 128, SA.shape, generator=g) + 1) << 12
+        pick = torch.randint(0, 3, SA.shape, generator=g) == 0
+        e = torch.randint(-4, 4, SA.shape, generator=g).float()
+        return ((1.0 + torch.where(pick, ties, m).double() / (1 << 20)) * torch.exp2(e.double())).float()
+
+    _codes_case(gpu_lib, MIXED, 256, 384, 13, layout=layout, exact=True, a_fill=one_hot, sa_fill=sa_fill)
 
 
 def test_layouts_bit_identical_and_deterministic(gpu_lib):
