@@ -20,17 +20,20 @@ namespace w4a8 {
 // next group's weights load while the current group's are in use); only the
 // activation rows and the scales, which every wave needs, are staged in LDS
 // through direct global->LDS loads:
-//   X ring   : P2_NX slots x [128 rows][128 B]  (row chunk c at c ^ xkey(row))
+//   X ring   : 6 slots (three pairs of groups) x [128 rows][128 B]
+//              (row chunk c at c ^ xkey(row))
 //   SB chunk : 2 x [512 cols][SC] u32  (E8M0 codes of groups SC*c .. SC*c+3,
 //              word gg of column n at gg ^ skey(n))
 //   SA chunk : 2 x [128 rows][SC] fp32 (word gg of row r at gg ^ skey(r))
-// Stage s (one K group): wait until the weights of group s (and everything
-// issued before them) have landed, barrier, issue the weights of group s + 1,
-// the scale chunk that group s + 2 opens (if any) and the activation rows of
-// group s + 2, then the 32 MFMAs of the group.  One in-order counter per wave
-// sets the depths: waiting for the weights of group s also waits for
-// everything issued before them, so the activation rows, issued last, run one
-// stage further ahead.
+// The K loop runs in pairs of groups with one barrier per pair (a barrier per
+// group measured 2-3% slower): wait for the weights of the pair's first group,
+// barrier, its 32 MFMAs; wait for the weights of the second group, issue the
+// activation rows of the two groups four ahead, the scale chunk they open (if
+// any) and the weights of the next pair's first group into the register slot
+// just used; the second group's MFMAs; the weights of the next pair's second
+// group.  Each weight load has one group of lead, each activation load one
+// and a half pairs.  One in-order counter per wave: every wait is counted
+// from the issue order (see pair()).
 // Per 128-K group a workgroup reads 32 KB of weights and 16 KB of activations
 // for 256 MFMAs, the fewest bytes per MFMA of the tile shapes whose
 // accumulators fit two waves per SIMD.
@@ -39,8 +42,7 @@ constexpr int MF_THREADS = 512;
 constexpr int MF_WAVES = MF_THREADS / 64;
 constexpr int MF_BN = TN_MFMA;          // 512 weight columns
 constexpr int MF_BM = T_MAX;            // 128 activation rows
-constexpr int P2_DX = 2;                // activation groups ahead (weights: one)
-constexpr int P2_NX = P2_DX + 1;        // activation ring slots
+constexpr int P2_NX = 6;                // activation ring slots: three pairs of groups
 constexpr int P2_XSLOT = MF_BM * 128;   // 16 KB
 constexpr int P2_SB = P2_NX * P2_XSLOT;
 constexpr int P2_SBBUF = MF_BN * SC * 4;  // 8 KB
@@ -52,9 +54,10 @@ static_assert(MF_BN == 64 * MF_WAVES, "each wave owns 64 columns");
 static_assert(P2_X_OPS * 1024 * MF_WAVES == MF_BM * 128, "activation loads cover the slot");
 static_assert(MF_BN * SC == MF_WAVES * 4 * 64, "four 4-byte E8M0 loads per lane cover a chunk");
 static_assert(MF_BM * SC == MF_WAVES * 64, "one 4-byte activation-scale load per lane covers a chunk");
-// a scale buffer is refilled P2_DX stages ahead, after every stage of the
-// chunk two back has passed the barrier of the stage that refills it
-static_assert(P2_DX <= SC, "scale chunk reuse distance");
+// a scale chunk (two pairs) is refilled during the pair two before its first
+// one, after every pair of the chunk two back has passed that pair's barrier
+static_assert(SC == 4, "a scale chunk is two pairs of groups");
+
 
 // LDS addresses of this lane's fragments in a stage slot / scale buffer: row
 // block mi adds the immediate mi * 2048 (X) or mi * 256 (SA).  Row m = 16 mi
@@ -151,18 +154,6 @@ struct MfmaTile {
     vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P2_SA + (c & 1) * P2_SABUF + wave * 256));
   }
 
-  // The loads issued at stage s, in issue order: the weights of group s + 1,
-  // the scale chunk that group s + 2 opens (if any), the activation rows of
-  // group s + 2.  Stages past the last group issue them with no lanes, so every
-  // stage issues the same loads and every wait is one constant.
-  __device__ __forceinline__ void issue(int s, v4i (&wnext)[4]) const {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) load_w(wnext[nb], nb, s + 1);
-    if (s + 2 < G && (s + 2) % SC == 0) load_scales((s + 2) / SC);
-#pragma unroll
-    for (int i = 0; i < P2_X_OPS; ++i) load_x(i, s + 2);
-  }
-
   // One K group: step mi issues the LDS reads of block mi+1 and the four
   // MFMAs of block mi; after each MFMA come the four promotion FMAs of the
   // partial two MFMAs back (the last two partials of a group are carried into
@@ -206,35 +197,61 @@ struct MfmaTile {
     }
   }
 
-  // Stage s: the weights of group s and everything issued before them have
-  // landed once at most the P2_X_OPS newest loads (the activation rows of
-  // group s + 1) are in flight
-  __device__ __forceinline__ void stage(int s, v4i (&wcur)[4], v4i (&wnext)[4], v4f (&acc)[8][4],
-                                        v4f (&pq)[2], float& sprev) {
-    wait_vm<P2_X_OPS>();
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) tie(wcur[nb]);
-    wg_barrier();
-    issue(s, wnext);
-    const uint8_t* slot = lds + (s % P2_NX) * P2_XSLOT;
-    const uint8_t* sbb = lds + P2_SB + ((s / SC) & 1) * P2_SBBUF;
-    const uint8_t* sab = lds + P2_SA + ((s / SC) & 1) * P2_SABUF;
-    const int gg = s % SC;
-    // column wn*64 + 16 nb + r16 (and row r16 + 16 mi) has scale key
-    // ((2 nb) & 3) ^ (r16 >> 3) (((2 mi) & 3) ^ (r16 >> 3))
+  // Operand pointers of group g for this lane.
+  __device__ __forceinline__ void group_ptrs(int g, P2Lds& a, int (&sbv)[4]) const {
+    const uint8_t* slot = lds + (g % P2_NX) * P2_XSLOT;
+    const uint8_t* sbb = lds + P2_SB + ((g / SC) & 1) * P2_SBBUF;
+    const uint8_t* sab = lds + P2_SA + ((g / SC) & 1) * P2_SABUF;
+    const int gg = g % SC;
     const int k0 = gg ^ (r16 >> 3);
     const uint8_t* sbl0 = sbb + ((wn * 64 + r16) * SC + k0) * 4;
     const uint8_t* sbl1 = sbb + ((wn * 64 + r16) * SC + (k0 ^ 2)) * 4;
-    int sbv[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       sbv[nb] = (int)((lds32(((nb & 1) ? sbl1 : sbl0) + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
-    P2Lds a;
     a.x0 = slot + xl0;
     a.x1 = slot + xl1;
     a.sa0 = sab + (r16 * SC + k0) * 4;
     a.sa1 = sab + (r16 * SC + (k0 ^ 2)) * 4;
-    if (wvalid) group(acc, pq, sprev, wcur, a, sbv);
+  }
+
+  // Pair t = groups 2t and 2t+1, one barrier.  Issue order: after group 2t,
+  // activation rows of groups 2t+4, 2t+5 (ring slots of pair t-1, which every
+  // wave finished before this pair's barrier), the scale chunk group 2t+4
+  // opens, the weights of 2t+2 (into w0, free now); after group 2t+1, the
+  // weights of 2t+3.  So at the start of pair t+1 only the weights of 2t+3
+  // may still be in flight (wait for at most 4), and before group 2t+3
+  // nothing newer than them was issued (wait for 0).  Loads past the last
+  // group run with exec = 0 from clamped addresses.
+  __device__ __forceinline__ void pair(int t, v4i (&w0)[4], v4i (&w1)[4], v4f (&acc)[8][4], v4f (&pq)[2],
+                                       float& sprev) {
+    const int g0 = 2 * t, g1 = 2 * t + 1;
+    wait_vm<4>();  // weights of g0 (only those of g1 may be in flight)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) tie(w0[nb]);
+    wg_barrier();
+    P2Lds a;
+    int sbv[4];
+    if (wvalid) {
+      group_ptrs(g0, a, sbv);
+      group(acc, pq, sprev, w0, a, sbv);
+    }
+    wait_vm<0>();  // weights of g1
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) tie(w1[nb]);
+#pragma unroll
+    for (int i = 0; i < P2_X_OPS; ++i) load_x(i, g0 + 4);
+#pragma unroll
+    for (int i = 0; i < P2_X_OPS; ++i) load_x(i, g1 + 4);
+    if (g0 + 4 < G && (g0 + 4) % SC == 0) load_scales((g0 + 4) / SC);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) load_w(w0[nb], nb, g0 + 2);
+    if (wvalid && g1 < G) {
+      group_ptrs(g1, a, sbv);
+      group(acc, pq, sprev, w1, a, sbv);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) load_w(w1[nb], nb, g1 + 2);
   }
 
   __device__ __forceinline__ void run() {
@@ -261,19 +278,19 @@ struct MfmaTile {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) w0[nb] = w1[nb] = v4i{0, 0, 0, 0};
 
-    // prologue: the loads of stages -2 and -1 (weights of group 0 land in w0;
-    // the weights "of group -1" are issued with no lanes, to keep the counts
-    // of every stage equal)
-    issue(-2, w1);
-    issue(-1, w0);
-    // whole pairs of stages, then the last odd one: no control-flow path
-    // skips a stage and then runs a later one
-    int s = 0;
-    for (; s + 2 <= G; s += 2) {
-      stage(s, w0, w1, acc, pq, sprev);
-      stage(s + 1, w1, w0, acc, pq, sprev);
-    }
-    if (s < G) stage(s, w0, w1, acc, pq, sprev);
+    // prologue: activation rows of groups 0-3, scale chunk 0, weights of
+    // groups 0 and 1
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < P2_X_OPS; ++i) load_x(i, g);
+    load_scales(0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) load_w(w0[nb], nb, 0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) load_w(w1[nb], nb, 1);
+    const int P = (G + 1) / 2;
+    for (int t = 0; t < P; ++t) pair(t, w0, w1, acc, pq, sprev);
     wait_vm<0>();  // every load has retired; the ties keep their registers reserved until here
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
