@@ -79,28 +79,35 @@ grouped_gemm_kernel(GemmArgs p) {
     }
   }
 
-  // phase 2: MFMA tiles, one workgroup each
+  // phase 2: MFMA tiles, one workgroup each; each tile issues the first
+  // shared-operand loads of the workgroup's next tile before its epilogue
   {
     // MT <= R / 65 + E and NT <= 2^31 / 512 keep the item count in 32 bits
     const int MT = uniform(s_mbase[p.E]);
     const int NT = (p.N + MF_BN - 1) / MF_BN;
     const int items = MT * NT;
     const int grid = gridDim.x;
-    const int rounds = (items + grid - 1) / grid;
-    for (int r = 0; r < rounds; ++r) {
+    // this workgroup's round-r tile; invalid past its last one (item numbers
+    // grow with r)
+    auto tile_of = [&](int r) -> TileCoord {
+      TileCoord t{0, 0, 0, 0, false};
       const int L = xcd_item(r, blockIdx.x, grid);
-      if (L >= items) continue;
+      if (L >= items) return t;
       int mt, nt;
       item_tile(L, MT, NT, &mt, &nt);
-      const int e = uniform(expert_of_tile(s_mbase, p.E, mt));
-      const int j = mt - uniform(s_mbase[e]);
-      const int base = uniform(s_off[e]);
-      const int rows_e = uniform(s_off[e + 1]) - base;
+      t.e = uniform(expert_of_tile(s_mbase, p.E, mt));
+      const int j = mt - uniform(s_mbase[t.e]);
+      const int base = uniform(s_off[t.e]);
+      const int rows_e = uniform(s_off[t.e + 1]) - base;
       const TileChoice tc = tile_rule(rows_e);
-      const int row0 = base + j * tc.tile_m;
-      const int rows = min(tc.tile_m, rows_e - j * tc.tile_m);
-      mfma_tile(p, lds, e, row0, rows, nt * MF_BN, R);
-    }
+      t.row0 = base + j * tc.tile_m;
+      t.rows = min(tc.tile_m, rows_e - j * tc.tile_m);
+      t.n0 = nt * MF_BN;
+      t.valid = true;
+      return t;
+    };
+    TileCoord t = tile_of(0);
+    for (int r = 0; t.valid; ++r) t = mfma_tile(p, lds, t, R, r > 0, [&]() { return tile_of(r + 1); });
   }
 }
 

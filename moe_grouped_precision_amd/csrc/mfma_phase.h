@@ -77,6 +77,12 @@ __device__ __forceinline__ void p2_read_x(const P2Lds& a, int mi, v4i& x0, v4i& 
   sa = ldsf(((mi & 1) ? a.sa1 : a.sa0) + mi * 16 * SC * 4);
 }
 
+// Coordinates of an MFMA tile: expert, first row, rows, first column.
+struct TileCoord {
+  int e, row0, rows, n0;
+  bool valid;
+};
+
 template <int NMB>
 struct MfmaTile {
   const GemmArgs& p;
@@ -254,7 +260,26 @@ struct MfmaTile {
     for (int nb = 0; nb < 4; ++nb) load_w(w1[nb], nb, g1 + 2);
   }
 
-  __device__ __forceinline__ void run() {
+  // The first shared-operand loads of this tile: activation rows of groups
+  // 0-3 into ring slots 0-3 and scale chunk 0.  The workgroup's previous tile
+  // issues them before its epilogue (so they land while it stores), or the
+  // tile itself if it is the workgroup's first.  They hold no registers.
+  __device__ __forceinline__ void prologue_shared() const {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < P2_X_OPS; ++i) load_x(i, g);
+    load_scales(0);
+  }
+
+  // The K loop of this tile (its shared-operand prologue issued already if
+  // shared_ready), then, once every wave is done with the ring, the shared-
+  // operand prologue of the workgroup's next tile (next() gives its
+  // coordinates, valid == false if there is none; it is called only after
+  // the K loop, so its results are not live across it), then the bf16
+  // epilogue of this one.  Returns the next tile's coordinates.
+  template <class Next>
+  __device__ __forceinline__ TileCoord run(bool shared_ready, Next next) {
     // zero accumulators, made opaque so that the compiler does not peel the
     // first K group to specialise it for zero inputs (a second copy of the
     // loop body with its own register assignment)
@@ -277,14 +302,10 @@ struct MfmaTile {
     v4i w0[4], w1[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) w0[nb] = w1[nb] = v4i{0, 0, 0, 0};
-
-    // prologue: activation rows of groups 0-3, scale chunk 0, weights of
-    // groups 0 and 1
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int i = 0; i < P2_X_OPS; ++i) load_x(i, g);
-    load_scales(0);
+    // prologue: activation rows of groups 0-3 and scale chunk 0 (unless the
+    // previous tile issued them), weights of groups 0 and 1 -- the loads the
+    // first pair's waits count
+    if (!shared_ready) prologue_shared();
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) load_w(w0[nb], nb, 0);
 #pragma unroll
@@ -300,6 +321,11 @@ struct MfmaTile {
     promote(acc[NMB - 1][2], sprev, pq[0]);
     promote(acc[NMB - 1][3], sprev, pq[1]);
     __syncthreads();  // every wave is done with the ring before the next tile's loads
+    // (the epilogue's stores, issued after these loads, only make the next
+    // tile's first wait, which counts the newest operations, wait for more
+    // than it needs)
+    const TileCoord nt = next();
+    if (nt.valid) MfmaTile<1>(p, lds, nt.e, nt.row0, nt.rows, nt.n0, R).prologue_shared();
 
     if (wvalid) {
       // lane coordinates recomputed (opaque) rather than kept live through the K loop
@@ -321,20 +347,22 @@ struct MfmaTile {
         }
       }
     }
+    return nt;
   }
 };
 
-__device__ __forceinline__ void mfma_tile(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
-                                          int n0, int R) {
-  switch ((rows + 15) >> 4) {
-    case 1: MfmaTile<1>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 2: MfmaTile<2>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 3: MfmaTile<3>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 4: MfmaTile<4>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 5: MfmaTile<5>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 6: MfmaTile<6>(p, lds, e, row0, rows, n0, R).run(); break;
-    case 7: MfmaTile<7>(p, lds, e, row0, rows, n0, R).run(); break;
-    default: MfmaTile<8>(p, lds, e, row0, rows, n0, R).run(); break;
+template <class Next>
+__device__ __forceinline__ TileCoord mfma_tile(const GemmArgs& p, uint8_t* lds, const TileCoord& t, int R,
+                                               bool shared_ready, Next next) {
+  switch ((t.rows + 15) >> 4) {
+    case 1: return MfmaTile<1>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 2: return MfmaTile<2>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 3: return MfmaTile<3>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 4: return MfmaTile<4>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 5: return MfmaTile<5>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 6: return MfmaTile<6>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 7: return MfmaTile<7>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    default: return MfmaTile<8>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
   }
 }
 
