@@ -28,6 +28,8 @@ grouped_gemm_kernel(GemmArgs p) {
   __shared__ int s_sbase[MAX_EXPERTS + 1];
   __shared__ int s_mbase[MAX_EXPERTS + 1];
   __shared__ int s_info[3];
+  __shared__ int s_ibase[MAX_EXPERTS + 1];
+  __shared__ int s_rr[1];
   if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info)) return;
   const int R = uniform(s_off[p.E]);
 
@@ -45,36 +47,27 @@ grouped_gemm_kernel(GemmArgs p) {
       while (u < u_end) {
         const int mt = (int)(u / nu);
         const int c0 = (int)(u - (long long)mt * nu);
-        const int w = (int)min((long long)min(P1_MAXNBW, nu - c0), u_end - u);
+        const int w = (int)min((long long)min(P1_RANGE_MAXNBW, nu - c0), u_end - u);
         const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
         const int row0 = uniform(s_off[e]);
         const int rows = uniform(s_off[e + 1]) - row0;
-        switch (w) {
-          case 1: stream_item<1>(p, lds, e, row0, rows, c0 * 64, R); break;
-          case 2: stream_item<2>(p, lds, e, row0, rows, c0 * 64, R); break;
-          default: stream_item<3>(p, lds, e, row0, rows, c0 * 64, R); break;
-        }
+        stream_item(p, lds, e, row0, rows, c0 * 64, w, R);
         u += w;
       }
-    } else {
-      // tiles of different row counts cost different amounts per column:
-      // items of one width dealt round-robin, so a workgroup's items come from
-      // several experts
-      const int nbw = stream_width_blocks(tiles, p.N, gridDim.x);
-      const int width = 64 * nbw;
-      const int nchunks = (p.N + width - 1) / width;
-      const long long items = (long long)tiles * nchunks;
-      for (long long it = blockIdx.x; it < items; it += gridDim.x) {
-        const int mt = (int)(it / nchunks);
-        const int n0 = (int)(it % nchunks) * width;
-        const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
+    } else if (tiles > 0) {
+      // tiles of different row blocks: items dealt round-robin, so a
+      // workgroup's items come from several experts; each expert's items are
+      // as wide as its row blocks allow, up to the cap the plan picks
+      stream_rr_plan(s_off, p.E, nu, gridDim.x, s_ibase, s_rr);
+      const int W = uniform(s_rr[0]);
+      const int items = uniform(s_ibase[p.E]);
+      for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int e = uniform(expert_of_tile(s_ibase, p.E, it));
         const int row0 = uniform(s_off[e]);
         const int rows = uniform(s_off[e + 1]) - row0;
-        switch (nbw) {
-          case 1: stream_item<1>(p, lds, e, row0, rows, n0, R); break;
-          case 2: stream_item<2>(p, lds, e, row0, rows, n0, R); break;
-          default: stream_item<3>(p, lds, e, row0, rows, n0, R); break;
-        }
+        const int we = min(W, stream_max_nbw((rows + 15) >> 4));
+        const int c0 = (it - uniform(s_ibase[e])) * we;
+        stream_item(p, lds, e, row0, rows, c0 * 64, min(we, nu - c0), R);
       }
     }
   }

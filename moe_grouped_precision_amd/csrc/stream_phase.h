@@ -35,7 +35,7 @@ namespace w4a8 {
 // are shared by the workgroup and come through LDS:
 //   X ring   : D+1 slots x [KG][2 halves][64 rows][128 B] @ 0  (row chunk c at c ^ (row & 7))
 //   SB chunk : 2 x [2 halves][64*NBW cols][SC] u32            @ P1_SB
-//   SA chunk : 2 x [2 halves][64 rows][SC] fp32               @ P1_SA
+//   SA chunk : 2 x [2 halves][64 rows][SC] fp32               @ P1_SB + 2 * SBS
 // Stage s: wait (the weights of stage s and, older, its activation rows have
 // landed), barrier, issue the activation rows of stage s + D, MFMAs, then the
 // weights of stage s + D into the register slot just used.  After the K loop
@@ -44,17 +44,24 @@ namespace w4a8 {
 // ---------------------------------------------------------------------------
 constexpr int P1_XGROUP = 16384;          // activation rows of one group, both halves
 constexpr int P1_XRING = 6 * P1_XGROUP;   // (D+1)*KG groups, at most 96 KB
-constexpr int P1_MAXNBW = 3;
+// widest item in 64-column units, per row blocks of the expert (the weight
+// ring, 16*NBW registers, and the accumulators, 4*NBW*MB, share the
+// register file with the MFMA operands)
+constexpr int P1_MAXNBW = 4;
+__host__ __device__ constexpr int stream_max_nbw(int mb) { return mb <= 2 ? 4 : 3; }
+// items of a contiguous range are at most this wide (wider measured no faster)
+constexpr int P1_RANGE_MAXNBW = 3;
 // groups of K per streaming stage: two halve the per-stage barriers and LDS
 // round trips against one, at the same bytes in flight (four, with a single
 // stage in flight, measured slower)
 constexpr int P1_KG = 2;
 constexpr int P1_SB = P1_XRING;
-constexpr int P1_SBBUF = 2 * 64 * P1_MAXNBW * SC * 4;      // 6 KB
-constexpr int P1_SA = P1_SB + 2 * P1_SBBUF;
+// SB chunk buffers are max(6 KB, NBW * 2 KB) apart: items up to three units
+// wide keep the 6 KB spacing (an 8 KB spacing measured 5% slower for them)
+__host__ __device__ constexpr int stream_sb_stride(int nbw) { return nbw <= 3 ? 6144 : 2048 * nbw; }
+constexpr int P1_SBMAX = 2 * stream_sb_stride(P1_MAXNBW);
 constexpr int P1_SABUF = 2 * 64 * SC * 4;                  // 2 KB
-constexpr int P1_BYTES = P1_SA + 2 * P1_SABUF;
-static_assert(P1_MAXNBW * 16384 <= P1_SB, "reduction scratch must fit below the scale chunks");
+constexpr int P1_BYTES = P1_SB + P1_SBMAX + 2 * P1_SABUF;
 
 template <int NBW, int KG, int MB>
 struct StreamItem {
@@ -70,6 +77,11 @@ struct StreamItem {
   // chunk after next: every stage of the chunk before must be done by then
   static_assert(SC % KG == 0 && D * KG <= SC, "scale chunk reuse distance");
   static_assert(KG == 2, "a stage's weight loads cover one 128-byte line (two groups) per column");
+  static_assert(NBW <= stream_max_nbw(MB), "register budget");
+  static constexpr int SBS = stream_sb_stride(NBW);  // SB chunk buffer spacing
+  static constexpr int SAB = P1_SB + 2 * SBS;        // SA chunk buffers
+  static_assert(SBS >= 2 * 64 * NBW * SC * 4 && SAB + 2 * P1_SABUF <= P1_BYTES, "scale chunk buffers");
+  static_assert(4 * NBW * MB * 1024 <= P1_SB, "reduction scratch must fit below the scale chunks");
 
   // Activation rows of stage s: 8*MB loads of 4 rows x 128 B per group, MB per
   // wave (half a wave each).  xt = the item's first row.
@@ -105,14 +117,14 @@ struct StreamItem {
       const int n = min(n0 + col, N - 1);
       const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
       vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-              lds_u32(lds + P1_SB + (c & 1) * P1_SBBUF + (wave * NBW + i) * 256));
+              lds_u32(lds + P1_SB + (c & 1) * SBS + (wave * NBW + i) * 256));
     }
     {
       const int idx = wave * 64 + lane;  // [h][row][gg]
       const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
       const size_t row = (size_t)row0 + min(r, rows - 1);
       const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
-      vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P1_SA + (c & 1) * P1_SABUF + wave * 256));
+      vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + SAB + (c & 1) * P1_SABUF + wave * 256));
     }
   }
 
@@ -230,8 +242,8 @@ struct StreamItem {
       for (int kg = 0; kg < KG; ++kg) {
         const int gl = s * KG + kg;  // group index within this wave's half
         if (gl < gcount) {
-          const uint8_t* sbb = lds + P1_SB + ((gl / SC) & 1) * P1_SBBUF;
-          const uint8_t* sab = lds + P1_SA + ((gl / SC) & 1) * P1_SABUF;
+          const uint8_t* sbb = lds + P1_SB + ((gl / SC) & 1) * SBS;
+          const uint8_t* sab = lds + SAB + ((gl / SC) & 1) * P1_SABUF;
           const int gg = gl % SC;
           int sbv[NBW];
 #pragma unroll
@@ -281,7 +293,7 @@ struct StreamItem {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < MB; ++i) red[((wn * NBW + j) * 4 + i) * 64 + lane] = acc[j][i];
+        for (int i = 0; i < MB; ++i) red[((wn * NBW + j) * MB + i) * 64 + lane] = acc[j][i];
     }
     __syncthreads();
     if (kh == 0) {
@@ -293,7 +305,7 @@ struct StreamItem {
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
             const int n = n0 + (wn * NBW + j) * 16 + q * 4;
-            const v4f o = red[((wn * NBW + j) * 4 + i) * 64 + lane];
+            const v4f o = red[((wn * NBW + j) * MB + i) * 64 + lane];
             if (n < N) store_bf16x4(crow + n, acc[j][i] + o);
           }
         }
@@ -303,35 +315,99 @@ struct StreamItem {
   }
 };
 
-template <int NBW>
-__device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
-                                            int n0, int R) {
-  switch ((rows + 15) >> 4) {
-    case 1: StreamItem<NBW, P1_KG, 1>::run(p, lds, e, row0, rows, n0, R); break;
-    case 2: StreamItem<NBW, P1_KG, 2>::run(p, lds, e, row0, rows, n0, R); break;
-    case 3: StreamItem<NBW, P1_KG, 3>::run(p, lds, e, row0, rows, n0, R); break;
-    default: StreamItem<NBW, P1_KG, 4>::run(p, lds, e, row0, rows, n0, R); break;
+template <int MB>
+__device__ __forceinline__ void stream_item_mb(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows, int n0,
+                                               int nbw, int R) {
+  switch (nbw) {
+    case 1: StreamItem<1, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
+    case 2: StreamItem<2, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
+    case 3: StreamItem<3, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
+    default: if constexpr (stream_max_nbw(MB) >= 4) StreamItem<4, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
   }
 }
 
-// Item width for the streaming phase, when items are dealt round-robin: the
-// width (64*NBW columns) that minimises rounds x per-item bytes, per-item
-// bytes ~ weights (32*NBW per K) plus activation rows (about 32 per K).  Wider
-// items re-read the activation rows less often; narrower items spread few
-// experts over more workgroups.
-__device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
-  int best = 1;
-  long long best_cost = -1;
-  for (int nbw = 1; nbw <= P1_MAXNBW; ++nbw) {
-    const long long items = (long long)tiles * ((N + 64 * nbw - 1) / (64 * nbw));
-    const long long rounds = (items + grid - 1) / grid;
-    const long long cost = rounds * (32LL * nbw + 32);
-    if (best_cost < 0 || cost <= best_cost) {
-      best_cost = cost;
-      best = nbw;
+// One streaming item of nbw units (nbw <= stream_max_nbw of its row blocks).
+__device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows, int n0,
+                                            int nbw, int R) {
+  switch ((rows + 15) >> 4) {
+    case 1: stream_item_mb<1>(p, lds, e, row0, rows, n0, nbw, R); break;
+    case 2: stream_item_mb<2>(p, lds, e, row0, rows, n0, nbw, R); break;
+    case 3: stream_item_mb<3>(p, lds, e, row0, rows, n0, nbw, R); break;
+    default: stream_item_mb<4>(p, lds, e, row0, rows, n0, nbw, R); break;
+  }
+}
+
+// Items dealt round-robin (experts of different row blocks): expert e's
+// items are w_e = min(W, stream_max_nbw(its row blocks)) units wide, with the
+// cap W that minimises rounds x per-item bytes, per-item bytes ~ weights (32
+// per unit per K) plus activation rows (about 32 per K).  Wider items re-read
+// the activation rows less often and pay the pipeline fill and drain fewer
+// times; narrower ones spread few experts over more workgroups.  Wave 0
+// writes s_ibase[e] = first item of expert e ([E] = total) and returns W in
+// s_rr[0]; every thread must call it.
+__device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, int grid, int* s_ibase, int* s_rr) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (E + 63) / 64;
+    const int i0 = lane * per;
+    int cnt[P1_MAXNBW];
+#pragma unroll
+    for (int w = 0; w < P1_MAXNBW; ++w) cnt[w] = 0;
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int wm = stream_max_nbw((rows + 15) >> 4);
+#pragma unroll
+          for (int w = 0; w < P1_MAXNBW; ++w) {
+            const int we = min(w + 1, wm);
+            cnt[w] += (nu + we - 1) / we;
+          }
+        }
+      }
+    }
+    int best = 1;
+    long long best_cost = -1;
+#pragma unroll
+    for (int w = 0; w < P1_MAXNBW; ++w) {
+      const long long items = __builtin_amdgcn_readlane(wave_inclusive_sum(cnt[w]), 63);
+      const long long cost = (items + grid - 1) / grid * (32LL * (w + 1) + 32);
+      if (best_cost < 0 || cost <= best_cost) {
+        best_cost = cost;
+        best = w + 1;
+      }
+    }
+    int mine = 0;
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int we = min(best, stream_max_nbw((rows + 15) >> 4));
+          mine += (nu + we - 1) / we;
+        }
+      }
+    }
+    const int incl = wave_inclusive_sum(mine);
+    int run = incl - mine;
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        s_ibase[e] = run;
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int we = min(best, stream_max_nbw((rows + 15) >> 4));
+          run += (nu + we - 1) / we;
+        }
+      }
+    }
+    if (lane == 0) {
+      s_ibase[E] = __builtin_amdgcn_readlane(incl, 63);
+      s_rr[0] = best;
     }
   }
-  return best;
+  __syncthreads();
 }
 
 // Work split of the streaming phase when every streaming tile has the same
@@ -344,7 +420,7 @@ __device__ __forceinline__ int stream_width_blocks(int tiles, int N, int grid) {
 //                  (21 or 22 each at 12 tiles on 256 CUs) and splits its nu
 //                  units evenly among them: no range spans two experts;
 //   tiles >= grid: workgroup b gets units [U*b/grid, U*(b+1)/grid).
-// A range is run as items of at most P1_MAXNBW units that never span two
+// A range is run as items of at most P1_RANGE_MAXNBW units that never span two
 // experts.  Against dealing fixed 192-column items round-robin this lowers
 // the largest share (E=12, 64 routed rows, N=6144: 5 units instead of 6).
 __device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid, long long* u0, long long* u1) {

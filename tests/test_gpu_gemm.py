@@ -167,6 +167,10 @@ def test_layouts_bit_identical_and_deterministic(gpu_lib):
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+DECODE_ROWS = [0, 0, 1, 3, 5, 5, 6, 6, 7, 7, 7, 8, 9, 9, 11, 14, 15, 15, 16, 17, 19, 21, 21, 21, 25, 25, 26,
+               30, 33, 36, 40, 54]
+
+
 @pytest.mark.parametrize("counts,N,K", [
     ([3], 32, 128),                   # E = 1, one streaming item
     ([200], 96, 256),                 # E = 1, MFMA class, partial n-tile
@@ -175,6 +179,11 @@ def test_layouts_bit_identical_and_deterministic(gpu_lib):
     (list(range(0, 140, 7)), 256, 128),
     ([5] * 300, 192, 128),            # more streaming tiles than CUs, all one row block
     ([40] * 3 + [0] + [33] * 2, 8192, 256),  # equal row blocks: units split per expert
+    # decode-like skewed rows (1..4 row blocks): items dealt round-robin, four
+    # units wide for experts of up to 32 rows and three above, with a
+    # narrower last item per expert (62 units) or a half unit at N (4000)
+    (DECODE_ROWS, 3968, 256),
+    (DECODE_ROWS, 4000, 128),
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
