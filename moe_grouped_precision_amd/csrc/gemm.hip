@@ -28,8 +28,8 @@ grouped_gemm_kernel(GemmArgs p) {
   __shared__ int s_sbase[MAX_EXPERTS + 1];
   __shared__ int s_mbase[MAX_EXPERTS + 1];
   __shared__ int s_info[3];
-  __shared__ int s_ibase[MAX_EXPERTS + 1];
-  __shared__ int s_rr[1];
+  __shared__ int s_eord[MAX_EXPERTS];
+  __shared__ int s_rrc[5][4];
   if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info)) return;
   const int R = uniform(s_off[p.E]);
 
@@ -55,19 +55,25 @@ grouped_gemm_kernel(GemmArgs p) {
         u += w;
       }
     } else if (tiles > 0) {
-      // tiles of different row blocks: items dealt round-robin, so a
-      // workgroup's items come from several experts; each expert's items are
-      // as wide as its row blocks allow, up to the cap the plan picks
-      stream_rr_plan(s_off, p.E, nu, gridDim.x, s_ibase, s_rr);
-      const int W = uniform(s_rr[0]);
-      const int items = uniform(s_ibase[p.E]);
-      for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int e = uniform(expert_of_tile(s_ibase, p.E, it));
+      // tiles of different row blocks: items dealt round-robin in a snake
+      // order of decreasing cost, each expert's items as wide as its row
+      // blocks allow up to the cap the plan picks
+      stream_rr_plan(s_off, p.E, nu, gridDim.x, s_eord, s_rrc);
+      const int items = uniform(s_rrc[4][0]);
+      const int G = gridDim.x;
+      for (int r = 0;; ++r) {
+        const int it = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+        if (it >= items) break;  // item numbers never decrease from one round to the next
+        int k = 0;
+        while (k < 3 && it >= uniform(s_rrc[k + 1][0])) ++k;
+        const int rel = it - uniform(s_rrc[k][0]);
+        const int ipe = uniform(s_rrc[k][2]), w = uniform(s_rrc[k][3]);
+        const int q = rel / ipe;
+        const int e = uniform(s_eord[uniform(s_rrc[k][1]) + q]);
         const int row0 = uniform(s_off[e]);
         const int rows = uniform(s_off[e + 1]) - row0;
-        const int we = min(W, stream_max_nbw((rows + 15) >> 4));
-        const int c0 = (it - uniform(s_ibase[e])) * we;
-        stream_item(p, lds, e, row0, rows, c0 * 64, min(we, nu - c0), R);
+        const int c0 = (rel - q * ipe) * w;
+        stream_item(p, lds, e, row0, rows, c0 * 64, min(w, nu - c0), R);
       }
     }
   }

@@ -337,74 +337,125 @@ __device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int
   }
 }
 
-// Items dealt round-robin (experts of different row blocks): expert e's
-// items are w_e = min(W, stream_max_nbw(its row blocks)) units wide, with the
+// Items dealt round-robin (experts of different row blocks).  Expert e's
+// items are w = min(W, stream_max_nbw(its row blocks)) units wide, with the
 // cap W that minimises rounds x per-item bytes, per-item bytes ~ weights (32
-// per unit per K) plus activation rows (about 32 per K).  Wider items re-read
+// per unit per K) plus activation rows (about 32 per K): wider items re-read
 // the activation rows less often and pay the pipeline fill and drain fewer
-// times; narrower ones spread few experts over more workgroups.  Wave 0
-// writes s_ibase[e] = first item of expert e ([E] = total) and returns W in
-// s_rr[0]; every thread must call it.
-__device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, int grid, int* s_ibase, int* s_rr) {
+// times, narrower ones spread few experts over more workgroups.  Items are
+// numbered in decreasing order of their cost, w * (4 + row blocks), in four
+// classes (the row blocks), and dealt in a snake order (round r gives
+// workgroup b item r*G + b for even r, r*G + G-1-b for odd r), so that a
+// workgroup's second item is light when its first was heavy.
+//   s_eord[k]   expert at class-ordered position k
+//   s_rrc[r]    class of rank r: {first item, first position, items per expert, width}
+//   s_rrc[4][0] total items
+// Wave 0 fills them; every thread must call it.
+__device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, int grid, int* s_eord,
+                                               int (*s_rrc)[4]) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 63) / 64;
     const int i0 = lane * per;
-    int cnt[P1_MAXNBW];
-#pragma unroll
-    for (int w = 0; w < P1_MAXNBW; ++w) cnt[w] = 0;
+    int cnt[4] = {0, 0, 0, 0};
     for (int k = 0; k < per; ++k) {
       const int e = i0 + k;
       if (e < E) {
         const int rows = s_off[e + 1] - s_off[e];
         if (rows > 0 && rows <= S_MAX) {
-          const int wm = stream_max_nbw((rows + 15) >> 4);
+          const int c = (rows - 1) >> 4;
 #pragma unroll
-          for (int w = 0; w < P1_MAXNBW; ++w) {
-            const int we = min(w + 1, wm);
-            cnt[w] += (nu + we - 1) / we;
-          }
+          for (int j = 0; j < 4; ++j) cnt[j] += j == c;
         }
       }
     }
-    int best = 1;
-    long long best_cost = -1;
+    int pre[4], tot[4];
 #pragma unroll
-    for (int w = 0; w < P1_MAXNBW; ++w) {
-      const long long items = __builtin_amdgcn_readlane(wave_inclusive_sum(cnt[w]), 63);
-      const long long cost = (items + grid - 1) / grid * (32LL * (w + 1) + 32);
+    for (int j = 0; j < 4; ++j) {
+      const int incl = wave_inclusive_sum(cnt[j]);
+      pre[j] = incl - cnt[j];
+      tot[j] = __builtin_amdgcn_readlane(incl, 63);
+    }
+    // the cap W
+    int W = 1;
+    long long best_cost = -1;
+    for (int w = 1; w <= P1_MAXNBW; ++w) {
+      long long items = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int we = min(w, stream_max_nbw(j + 1));
+        items += (long long)tot[j] * ((nu + we - 1) / we);
+      }
+      const long long cost = (items + grid - 1) / grid * (32LL * w + 32);
       if (best_cost < 0 || cost <= best_cost) {
         best_cost = cost;
-        best = w + 1;
+        W = w;
       }
     }
-    int mine = 0;
+    // classes ranked by decreasing item cost (ties: more row blocks first)
+    int rank_of[4], key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = min(W, stream_max_nbw(j + 1)) * (5 + j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int r = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r += key[i] > key[j] || (key[i] == key[j] && i > j);
+      rank_of[j] = r;
+    }
+    int pos0[4], item0[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pos0[j] = 0;
+      item0[j] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (rank_of[i] < rank_of[j]) {
+          const int wi = min(W, stream_max_nbw(i + 1));
+          pos0[j] += tot[i];
+          item0[j] += tot[i] * ((nu + wi - 1) / wi);
+        }
+    }
+    int next[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) next[j] = pos0[j] + pre[j];
     for (int k = 0; k < per; ++k) {
       const int e = i0 + k;
       if (e < E) {
         const int rows = s_off[e + 1] - s_off[e];
         if (rows > 0 && rows <= S_MAX) {
-          const int we = min(best, stream_max_nbw((rows + 15) >> 4));
-          mine += (nu + we - 1) / we;
+          const int c = (rows - 1) >> 4;
+          int pos = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j == c) pos = next[j]++;
+          s_eord[pos] = e;
         }
       }
     }
-    const int incl = wave_inclusive_sum(mine);
-    int run = incl - mine;
-    for (int k = 0; k < per; ++k) {
-      const int e = i0 + k;
-      if (e < E) {
-        s_ibase[e] = run;
-        const int rows = s_off[e + 1] - s_off[e];
-        if (rows > 0 && rows <= S_MAX) {
-          const int we = min(best, stream_max_nbw((rows + 15) >> 4));
-          run += (nu + we - 1) / we;
+    if (lane < 4) {
+      int j = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (rank_of[i] == lane) j = i;
+      int pj = 0, ij = 0, tj = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i == j) { pj = pos0[i]; ij = item0[i]; tj = tot[i]; }
+      const int wj = min(W, stream_max_nbw(j + 1));
+      s_rrc[lane][0] = ij;
+      s_rrc[lane][1] = pj;
+      s_rrc[lane][2] = tj > 0 ? (nu + wj - 1) / wj : 0;
+      s_rrc[lane][3] = wj;
+      if (lane == 0) {
+        long long items = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int wi = min(W, stream_max_nbw(i + 1));
+          items += (long long)tot[i] * ((nu + wi - 1) / wi);
         }
+        s_rrc[4][0] = (int)items;
       }
-    }
-    if (lane == 0) {
-      s_ibase[E] = __builtin_amdgcn_readlane(incl, 63);
-      s_rr[0] = best;
     }
   }
   __syncthreads();
