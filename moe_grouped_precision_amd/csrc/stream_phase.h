@@ -376,26 +376,33 @@ __device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, 
       pre[j] = incl - cnt[j];
       tot[j] = __builtin_amdgcn_readlane(incl, 63);
     }
-    // the cap W
+    // items per expert of width d = 1..4: ceil(nu / d), the thirds by a
+    // multiply-shift (exact for any 32-bit nu)
+    const int ipd[4] = {nu, (nu + 1) >> 1, (int)(((uint64_t)(uint32_t)(nu + 2) * 0xAAAAAAABull) >> 33), (nu + 3) >> 2};
+    static_assert(P1_MAXNBW == 4, "items per expert are tabulated for widths 1..4");
+    // the cap W (ties go to the wider cap); rounds by a float division,
+    // exact below 2^24 items
     int W = 1;
-    long long best_cost = -1;
-    for (int w = 1; w <= P1_MAXNBW; ++w) {
-      long long items = 0;
+    float best_cost = -1.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int we = min(w, stream_max_nbw(j + 1));
-        items += (long long)tot[j] * ((nu + we - 1) / we);
-      }
-      const long long cost = (items + grid - 1) / grid * (32LL * w + 32);
-      if (best_cost < 0 || cost <= best_cost) {
+    for (int w = 1; w <= P1_MAXNBW; ++w) {
+      int items = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) items += tot[j] * ipd[min(w, stream_max_nbw(j + 1)) - 1];
+      const float cost = ceilf((float)items / (float)grid) * (float)(32 * w + 32);
+      if (best_cost < 0.f || cost <= best_cost) {
         best_cost = cost;
         W = w;
       }
     }
     // classes ranked by decreasing item cost (ties: more row blocks first)
-    int rank_of[4], key[4];
+    int wd[4], ipe[4], key[4], rank_of[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = min(W, stream_max_nbw(j + 1)) * (5 + j);
+    for (int j = 0; j < 4; ++j) {
+      wd[j] = min(W, stream_max_nbw(j + 1));
+      ipe[j] = ipd[wd[j] - 1];
+      key[j] = wd[j] * (5 + j);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int r = 0;
@@ -403,17 +410,17 @@ __device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, 
       for (int i = 0; i < 4; ++i) r += key[i] > key[j] || (key[i] == key[j] && i > j);
       rank_of[j] = r;
     }
-    int pos0[4], item0[4];
+    int pos0[4], item0[4], total = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       pos0[j] = 0;
       item0[j] = 0;
+      total += tot[j] * ipe[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (rank_of[i] < rank_of[j]) {
-          const int wi = min(W, stream_max_nbw(i + 1));
           pos0[j] += tot[i];
-          item0[j] += tot[i] * ((nu + wi - 1) / wi);
+          item0[j] += tot[i] * ipe[i];
         }
     }
     int next[4];
@@ -433,30 +440,15 @@ __device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, 
         }
       }
     }
-    if (lane < 4) {
-      int j = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (rank_of[i] == lane) j = i;
-      int pj = 0, ij = 0, tj = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i == j) { pj = pos0[i]; ij = item0[i]; tj = tot[i]; }
-      const int wj = min(W, stream_max_nbw(j + 1));
-      s_rrc[lane][0] = ij;
-      s_rrc[lane][1] = pj;
-      s_rrc[lane][2] = tj > 0 ? (nu + wj - 1) / wj : 0;
-      s_rrc[lane][3] = wj;
-      if (lane == 0) {
-        long long items = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int wi = min(W, stream_max_nbw(i + 1));
-          items += (long long)tot[i] * ((nu + wi - 1) / wi);
-        }
-        s_rrc[4][0] = (int)items;
+    for (int j = 0; j < 4; ++j)
+      if (lane == rank_of[j]) {
+        s_rrc[lane][0] = item0[j];
+        s_rrc[lane][1] = pos0[j];
+        s_rrc[lane][2] = tot[j] > 0 ? ipe[j] : 0;
+        s_rrc[lane][3] = wd[j];
       }
-    }
+    if (lane == 0) s_rrc[4][0] = total;
   }
   __syncthreads();
 }
