@@ -21,6 +21,8 @@ Modules:
   gemm    -- the grouped GEMM above (fp64 BLAS per expert).
   route   -- routing histogram, exclusive-scan offsets, stable row map.
   plan    -- the per-expert tile rule and the tile list built from it.
+  quant   -- bf16 tokens -> E4M3 codes with per-(row, 128) amax/448 scales,
+             gathered to the grouped row of every slot.
 
 Parity status: no page prints a worked example or output value for any of
 these, so every function is pinned by closed forms, invariants, exact
@@ -39,3 +41,4 @@ from .formats import (  # noqa: F401
 from .gemm import expert_gemm_f64, grouped_gemm_bf16, grouped_gemm_f64, rows_gemm_f64  # noqa: F401
 from .plan import PLAN_PARAMS, plan_ref, tile_rule  # noqa: F401
 from .route import route_ref  # noqa: F401
+from .quant import bf16_bits_to_f32, e4m3_encode_rne, quantize_gather, quantize_tokens  # noqa: F401
