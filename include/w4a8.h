@@ -119,6 +119,33 @@ int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K,
               void* plan_dev, size_t plan_bytes, void* stream);
 
 /*
+ * w4a8_quantize_gather -- the producer of the GEMM's A and a_scales: bf16
+ * tokens quantized to E4M3 codes with one fp32 scale per (row, 128-K group)
+ * (humming PR #129, "Results" command: float8e4m3 activations, input-scale
+ * group size 128), written to the grouped row of every (token, slot).
+ *
+ * x_bf16_dev       uint16 (bf16 bits) [T][K], row-major.  16-byte aligned.
+ * row_of_slot_dev  int32 [T*top_k] (as produced by w4a8_route_prep): the
+ *                  grouped row of slot (t, j) at t*top_k + j.  Slots whose
+ *                  row is outside [0, R) are skipped.  4-byte aligned.
+ * A_fp8_dev        out uint8 [R][K] E4M3FN codes.  16-byte aligned.
+ * a_scales_dev     out fp32 per (row, group) in a_scale_layout
+ *                  (W4A8_SCALE_ROW_MAJOR [R][K/128] or W4A8_SCALE_M_MAJOR
+ *                  [K/128][R]).  4-byte aligned.
+ * Per token t and group g: s = amax|x[t, 128g .. 128g+127]| / 448 (1 if the
+ * group is all zero), code = E4M3FN round-to-nearest-even of clip(x / s,
+ * +-448), fp32 divisions rounded to nearest; sign kept (-0 -> 0x80).  Every
+ * named row gets the codes and scales of its token; other rows are left as
+ * they were.  NaN or infinite inputs are outside the definition.
+ * Limits: T >= 0, 1 <= top_k, T*top_k < 2^31, K % 128 == 0,
+ * 128 <= K <= W4A8_MAX_K, R >= 0.  T == 0 or R == 0 does nothing.
+ */
+int w4a8_quantize_gather(const uint16_t* x_bf16_dev, int T, int K,
+                         const int32_t* row_of_slot_dev, int top_k, int R,
+                         uint8_t* A_fp8_dev, float* a_scales_dev, int a_scale_layout,
+                         void* stream);
+
+/*
  * w4a8_grouped_gemm -- the grouped W4A8 GEMM.
  *
  * A_fp8_dev          uint8 [R][K] E4M3 codes; rows offsets[e]..offsets[e+1]-1

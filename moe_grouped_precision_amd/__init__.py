@@ -9,6 +9,7 @@ torch when the caller does not pass them.
     route_prep(topk_ids, E)          -> counts, expert_offsets, row_of_slot
     plan(expert_offsets, E, N, K)    -> int32 plan (header + tiles)
     grouped_gemm(A, SA, layout, B, SB, expert_offsets, out=None) -> C (bf16)
+    quantize_gather(x, row_of_slot, top_k, R, layout) -> A (E4M3 codes), SA
 """
 
 from ._lib import (  # noqa: F401
@@ -21,5 +22,6 @@ from ._lib import (  # noqa: F401
     plan,
     plan_bytes,
     plan_params,
+    quantize_gather,
     route_prep,
 )

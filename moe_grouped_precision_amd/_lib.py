@@ -40,6 +40,8 @@ def _declare(lib):
     lib.w4a8_plan.restype = i32
     lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_quantize_gather.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, i32, vp]
+    lib.w4a8_quantize_gather.restype = i32
     lib.w4a8_plan_params.argtypes = [ctypes.POINTER(ctypes.c_int32), i32]
     lib.w4a8_plan_params.restype = i32
     lib.w4a8_status_string.argtypes = [i32]
@@ -177,3 +179,28 @@ def grouped_gemm(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor
         _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
         _ptr(out), _stream()))
     return out
+
+
+def quantize_gather(x: torch.Tensor, row_of_slot: torch.Tensor, top_k: int, R: int, layout: int,
+                    A: Optional[torch.Tensor] = None, SA: Optional[torch.Tensor] = None):
+    """bf16 tokens x [T, K] -> (A uint8 [R, K] E4M3 codes, SA fp32 scales) written
+    to the grouped row of every slot (row_of_slot int32 [T * top_k]); SA is
+    [R, K/128] for layout 0 and [K/128, R] for layout 1."""
+    lib = load()
+    if x.dim() != 2:
+        raise ValueError("x must be [T, K]")
+    T, K = x.shape
+    if x.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("x must be bfloat16 (or 16-bit integer bits)")
+    _need(x, "x", x.dtype)
+    _need(row_of_slot, "row_of_slot", torch.int32, T * top_k)
+    if A is None:
+        A = torch.zeros((R, K), dtype=torch.uint8, device=x.device)
+    if SA is None:
+        shape = (R, K // 128) if layout == 0 else (K // 128, R)
+        SA = torch.zeros(shape, dtype=torch.float32, device=x.device)
+    _need(A, "A", torch.uint8, R * K)
+    _need(SA, "a_scales", torch.float32, R * (K // 128))
+    _check("w4a8_quantize_gather", lib.w4a8_quantize_gather(
+        _ptr(x), T, K, _ptr(row_of_slot), int(top_k), int(R), _ptr(A), _ptr(SA), int(layout), _stream()))
+    return A, SA

@@ -178,4 +178,27 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
   return ok();
 }
 
+int w4a8_quantize_gather(const uint16_t* x_bf16_dev, int T, int K, const int32_t* row_of_slot_dev, int top_k,
+                         int R, uint8_t* A_fp8_dev, float* a_scales_dev, int a_scale_layout, void* stream) {
+  if (T < 0 || top_k < 1 || R < 0) return fail(W4A8_ERR_SHAPE, "T=%d top_k=%d R=%d", T, top_k, R);
+  if ((int64_t)T * top_k >= (int64_t)1 << 31) return fail(W4A8_ERR_SHAPE, "T*top_k too large");
+  if (K < 128 || K % 128 || K > W4A8_MAX_K)
+    return fail(W4A8_ERR_SHAPE, "K=%d must be a multiple of 128 in [128, %d]", K, W4A8_MAX_K);
+  if (a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR)
+    return fail(W4A8_ERR_LAYOUT, "a_scale_layout=%d is neither row-major (0) nor M-major (1)", a_scale_layout);
+  if (T > 0 && (!x_bf16_dev || !row_of_slot_dev || (R > 0 && (!A_fp8_dev || !a_scales_dev))))
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(x_bf16_dev, 16) || !aligned(A_fp8_dev, 16) || !aligned(row_of_slot_dev, 4) ||
+      !aligned(a_scales_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "x and A need 16-byte, row_of_slot and scales 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  int st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  if (T == 0 || R == 0) return ok();
+  hipError_t e = w4a8::launch_quant_gather(x_bf16_dev, T, K, row_of_slot_dev, top_k, R, A_fp8_dev, a_scales_dev,
+                                           a_scale_layout, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "quantize_gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

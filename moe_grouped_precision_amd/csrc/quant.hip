@@ -1,0 +1,101 @@
+// Activation quantization with the gather into grouped rows, gfx950.
+//
+// bf16 tokens -> FP8 E4M3FN codes with one fp32 scale per (row, 128-K group),
+// written to the grouped row of every (token, slot): the producer of the
+// grouped GEMM's A and a_scales (humming PR #129, "Results" command:
+// float8e4m3 activations with input-scale group size 128, grouped_contiguous
+// rows).  Per group, s = amax / 448 (1 for an all-zero group), v =
+// clip(x / s, +-448) with IEEE fp32 divisions, code = round to nearest even
+// of v onto the E4M3FN grid (OCP 8-bit floating point: largest finite 448,
+// subnormals m/8 * 2^-6).
+//
+// The work is a stream: read 2 bytes per element once, write one byte per
+// element per slot.  One workgroup per token; 8 lanes per 128-element group,
+// 16 elements (two 16-byte loads) per lane, the group's amax by three lane
+// exchanges; a wave stores 8 consecutive groups = 1 KB of codes per slot in
+// one 16-byte store per lane.  No LDS, no barrier.  Like the cast kernels of
+// TransformerEngine PR #3459 (description: register-only rowwise cast, no
+// shared memory or barrier), nothing is staged; unlike them the scale is the
+// fp32 amax/448 of 128 elements, not an E8M0 exponent of 32.
+#include "w4a8_launch.h"
+
+#include <hip/hip_runtime.h>
+
+namespace w4a8 {
+namespace {
+
+// E4M3FN code of a finite v with |v| <= 448, round to nearest even, sign kept.
+// Below 2^-6 the grid is the multiples of 2^-9 (the product by 512 is exact
+// and rintf rounds halves to even; 8 * 2^-9 = 2^-6 is code 8).  Above, the
+// fp32 mantissa is cut to 3 bits with round to nearest even; a carry out of
+// the mantissa moves to the next exponent by the same addition.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7fffffffu;
+  uint32_t code;
+  if (a < 0x3c800000u) {
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t e = (a >> 23) - 120u;            // biased E4M3 exponent: (e32 - 127) + 7
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xfffffu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
+    code = (e << 3) + keep + up;
+  }
+  return code | sign;
+}
+
+__global__ void __launch_bounds__(256)
+quant_gather_kernel(const uint16_t* __restrict__ x, int K, const int32_t* __restrict__ row_of_slot,
+                    int top_k, int R, uint8_t* __restrict__ A, float* __restrict__ SA, int layout) {
+  const int t = blockIdx.x;
+  const int G = K >> 7;
+  const int lane8 = threadIdx.x & 7;       // position in the group
+  const int gsub = threadIdx.x >> 3;       // group slot, 32 per pass
+  const uint16_t* xt = x + (size_t)t * K;
+  const int32_t* rs = row_of_slot + (size_t)t * top_k;
+  for (int g = gsub; g < G; g += 32) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u* src = reinterpret_cast<const v4u*>(xt + g * 128 + lane8 * 16);
+    const v4u p = __builtin_nontemporal_load(src), q = __builtin_nontemporal_load(src + 1);
+    const uint32_t w[8] = {p[0], p[1], p[2], p[3], q[0], q[1], q[2], q[3]};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);            // element 2i: low half
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);  // element 2i+1: high half
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 8));
+    m = fmaxf(m, __shfl_xor(m, 2, 8));
+    m = fmaxf(m, __shfl_xor(m, 4, 8));
+    const float s = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = fminf(fmaxf(__fdiv_rn(v[i], s), -448.0f), 448.0f);
+      c[i >> 2] |= e4m3_rne(y) << (8 * (i & 3));
+    }
+    const uint4 out = make_uint4(c[0], c[1], c[2], c[3]);
+    for (int j = 0; j < top_k; ++j) {
+      const int r = rs[j];
+      if (r < 0 || r >= R) continue;  // a slot that names no row
+      *reinterpret_cast<uint4*>(A + (size_t)r * K + g * 128 + lane8 * 16) = out;
+      if (lane8 == 0) SA[layout ? (size_t)g * R + r : (size_t)r * G + g] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_gather(const uint16_t* x, int T, int K, const int32_t* row_of_slot, int top_k, int R,
+                               uint8_t* A, float* SA, int layout, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_gather_kernel, dim3(T), dim3(256), 0, stream, x, K, row_of_slot, top_k, R, A, SA,
+                     layout);
+  return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -23,5 +23,7 @@ hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int 
                        hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t grouped_gemm_occupancy(int* blocks);
+hipError_t launch_quant_gather(const uint16_t* x, int T, int K, const int32_t* row_of_slot, int top_k, int R,
+                               uint8_t* A, float* SA, int layout, hipStream_t stream);
 
 }  // namespace w4a8

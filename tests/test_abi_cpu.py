@@ -99,6 +99,20 @@ def test_plan_and_route_host_validation(lib):
     assert lib.w4a8_route_prep(ctypes.c_void_p((1 << 20) + 2), 4, 2, 8, P16, P16, P16, NUL) == 4
 
 
+def test_quantize_gather_host_validation(lib):
+    q = lib.w4a8_quantize_gather
+    assert q(P16, 4, 512, P16, 0, 8, P16, P16, 0, NUL) == 2        # top_k = 0
+    assert q(P16, -1, 512, P16, 2, 8, P16, P16, 0, NUL) == 2       # T < 0
+    assert q(P16, 4, 500, P16, 2, 8, P16, P16, 0, NUL) == 2        # K % 128
+    assert q(P16, 4, 512, P16, 2, -1, P16, P16, 0, NUL) == 2       # R < 0
+    assert q(P16, 4, 512, P16, 2, 8, P16, P16, 2, NUL) == 3        # bad layout
+    assert q(NUL, 4, 512, P16, 2, 8, P16, P16, 0, NUL) == 1        # null x
+    assert q(P16, 4, 512, P16, 2, 8, NUL, P16, 0, NUL) == 1        # null A
+    assert q(P4, 4, 512, P16, 2, 8, P16, P16, 0, NUL) == 4         # misaligned x
+    assert q(P16, 4, 512, P16, 2, 8, P4, P16, 0, NUL) == 4         # misaligned A
+    assert lib.w4a8_last_error() != b""
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():
