@@ -139,6 +139,46 @@ def cpu_baseline(p, off, layout, budget_s=20.0, min_s=10.0):
                       f"workload, {passes} pass(es), numpy fp64 oracle, {dt:.1f} s"}
 
 
+def measure_quantize_gather(reps=20, warmup=3):
+    """The activation quantizer with gather (w4a8_quantize_gather) on the large
+    prefill activations: 16384 bf16 tokens x 6144, top-8 biased routing over 32
+    experts, M-major scales.  Median of `reps` launches timed with HIP events
+    on the launch stream; HBM roofline on the bytes it must move."""
+    import numpy as np
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    cfg = synth.CONFIGS["prefill_gateup"]
+    T, K, E, k = cfg["T"], cfg["K"], cfg["E"], cfg["top_k"]
+    g = torch.Generator(device="cuda").manual_seed(17)
+    x = torch.randn((T, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    ids = synth.make_routing(cfg["routing"], T, E, k, cfg["seed"]).to("cuda")
+    _, off, ros = w4a8.route_prep(ids, E)
+    R = int(off[-1].item())
+    G = K // 128
+    A = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+    SA = torch.empty((G, R), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        w4a8.quantize_gather(x, ros, k, R, 1, A=A, SA=SA)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        w4a8.quantize_gather(x, ros, k, R, 1, A=A, SA=SA)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in ev])
+    nbytes = T * K * 2 + 4 * T * k + R * K + 4 * R * G
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{T} bf16 tokens x {K}, top-{k} {cfg['routing']} routing over {E} experts "
+                        f"({R} rows), M-major scales",
+            "us_median": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +190,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, HBM read bandwidth)")
+    ap.add_argument("--no-quantize", action="store_true",
+                    help="skip the activation-quantizer measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
@@ -258,6 +300,11 @@ def main():
         roof["measured_peak"] = measured
         roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
+    quant = None
+    if not args.no_quantize:
+        log("timing the activation quantizer with gather")
+        quant = measure_quantize_gather()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -292,6 +339,7 @@ def main():
         },
         "roofline": roof,
         "probes": probes,
+        "quantize_gather": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
