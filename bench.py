@@ -179,6 +179,44 @@ def measure_quantize_gather(reps=20, warmup=3):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measure_combine(reps=20, warmup=3):
+    """The top-k combine (w4a8_combine) on the prefill down-projection output:
+    1152 tokens, top-8 biased routing over 32 experts, 6144 bf16 columns.
+    Median of `reps` launches timed with HIP events on the launch stream; HBM
+    roofline on the bytes it must move."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    cfg = synth.CONFIGS["prefill_down"]
+    T, N, E, k = cfg["T"], cfg["N"], cfg["E"], cfg["top_k"]
+    g = torch.Generator(device="cuda").manual_seed(19)
+    ids = synth.make_routing(cfg["routing"], T, E, k, cfg["seed"]).to("cuda")
+    _, off, ros = w4a8.route_prep(ids, E)
+    R = int(off[-1].item())
+    C = torch.randn((R, N), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = torch.rand((T * k,), generator=g, device="cuda", dtype=torch.float32)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        w4a8.combine(C, ros, w, k, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        w4a8.combine(C, ros, w, k, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in ev])
+    nbytes = R * N * 2 + T * N * 2 + 8 * T * k
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{T} tokens x top-{k} rows of {N} bf16 columns ({R} rows), {cfg['routing']} routing "
+                        f"over {E} experts",
+            "us_median": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +229,7 @@ def main():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, HBM read bandwidth)")
     ap.add_argument("--no-quantize", action="store_true",
-                    help="skip the activation-quantizer measurement")
+                    help="skip the activation-quantizer and combine measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
@@ -300,10 +338,11 @@ def main():
         roof["measured_peak"] = measured
         roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
-    quant = None
+    quant = comb = None
     if not args.no_quantize:
-        log("timing the activation quantizer with gather")
+        log("timing the activation quantizer with gather and the top-k combine")
         quant = measure_quantize_gather()
+        comb = measure_combine()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,6 +379,7 @@ def main():
         "roofline": roof,
         "probes": probes,
         "quantize_gather": quant,
+        "combine": comb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -146,6 +146,28 @@ int w4a8_quantize_gather(const uint16_t* x_bf16_dev, int T, int K,
                          void* stream);
 
 /*
+ * w4a8_combine -- the step after the grouped GEMM: every token's top_k
+ * expert rows summed back, each weighted by its router weight (the
+ * single-GPU half of an expert-parallel combine; the routing it inverts is
+ * the MoE planning of MoonEP PR #38, background section).
+ *
+ * C_bf16_dev       uint16 (bf16 bits) [R][N], grouped rows.  16-byte aligned.
+ * row_of_slot_dev  int32 [T*top_k]: the row of slot (t, j) at t*top_k + j
+ *                  (as produced by w4a8_route_prep); rows outside [0, R)
+ *                  contribute nothing.  4-byte aligned.
+ * weights_dev      fp32 [T*top_k]: the weight of each slot.  4-byte aligned.
+ * out_bf16_dev     out uint16 (bf16 bits) [T][N].  16-byte aligned.
+ * out[t, :] = bf16_rne(sum over j = 0, 1, ..., top_k-1 of w[t, j] *
+ * C[row(t, j), :]), summed in fp32 in that order with one rounded product
+ * and one rounded addition per term (no fused multiply-add), from 0; a token
+ * with no valid slot gets zeros.  The result is unique.
+ * Limits: T >= 0, 1 <= top_k, T*top_k < 2^31, N % 8 == 0,
+ * 8 <= N <= W4A8_MAX_N, R >= 0.  T == 0 does nothing.
+ */
+int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of_slot_dev,
+                 const float* weights_dev, int T, int top_k, uint16_t* out_bf16_dev, void* stream);
+
+/*
  * w4a8_grouped_gemm -- the grouped W4A8 GEMM.
  *
  * A_fp8_dev          uint8 [R][K] E4M3 codes; rows offsets[e]..offsets[e+1]-1

@@ -10,12 +10,14 @@ torch when the caller does not pass them.
     plan(expert_offsets, E, N, K)    -> int32 plan (header + tiles)
     grouped_gemm(A, SA, layout, B, SB, expert_offsets, out=None) -> C (bf16)
     quantize_gather(x, row_of_slot, top_k, R, layout) -> A (E4M3 codes), SA
+    combine(C, row_of_slot, weights, top_k, out=None) -> per-token bf16 sums
 """
 
 from ._lib import (  # noqa: F401
     SCALE_M_MAJOR,
     SCALE_ROW_MAJOR,
     W4A8Error,
+    combine,
     grouped_gemm,
     lib_path,
     load,

@@ -40,6 +40,8 @@ def _declare(lib):
     lib.w4a8_plan.restype = i32
     lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_combine.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp]
+    lib.w4a8_combine.restype = i32
     lib.w4a8_quantize_gather.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, i32, vp]
     lib.w4a8_quantize_gather.restype = i32
     lib.w4a8_plan_params.argtypes = [ctypes.POINTER(ctypes.c_int32), i32]
@@ -204,3 +206,30 @@ def quantize_gather(x: torch.Tensor, row_of_slot: torch.Tensor, top_k: int, R: i
     _check("w4a8_quantize_gather", lib.w4a8_quantize_gather(
         _ptr(x), T, K, _ptr(row_of_slot), int(top_k), int(R), _ptr(A), _ptr(SA), int(layout), _stream()))
     return A, SA
+
+
+def combine(C: torch.Tensor, row_of_slot: torch.Tensor, weights: torch.Tensor, top_k: int,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t, :] (bf16) = sum_j weights[t*top_k + j] * C[row_of_slot[t*top_k + j], :],
+    fp32 in slot order; C [R, N] bf16 grouped rows, row_of_slot int32 and
+    weights fp32 of T*top_k slots."""
+    lib = load()
+    if C.dim() != 2:
+        raise ValueError("C must be [R, N]")
+    R, N = C.shape
+    if C.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("C must be bfloat16 (or 16-bit integer bits)")
+    _need(C, "C", C.dtype)
+    if row_of_slot.numel() % top_k:
+        raise ValueError("row_of_slot must hold T * top_k entries")
+    T = row_of_slot.numel() // top_k
+    _need(row_of_slot, "row_of_slot", torch.int32, T * top_k)
+    _need(weights, "weights", torch.float32, T * top_k)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=C.device)
+    if out.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("out must be bfloat16 (or 16-bit integer bits)")
+    _need(out, "out", out.dtype, T * N)
+    _check("w4a8_combine", lib.w4a8_combine(_ptr(C), R, N, _ptr(row_of_slot), _ptr(weights), T, int(top_k),
+                                            _ptr(out), _stream()))
+    return out

@@ -201,4 +201,24 @@ int w4a8_quantize_gather(const uint16_t* x_bf16_dev, int T, int K, const int32_t
   return ok();
 }
 
+int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of_slot_dev,
+                 const float* weights_dev, int T, int top_k, uint16_t* out_bf16_dev, void* stream) {
+  if (T < 0 || top_k < 1 || R < 0) return fail(W4A8_ERR_SHAPE, "T=%d top_k=%d R=%d", T, top_k, R);
+  if ((int64_t)T * top_k >= (int64_t)1 << 31) return fail(W4A8_ERR_SHAPE, "T*top_k too large");
+  if (N < 8 || N % 8 || N > W4A8_MAX_N) return fail(W4A8_ERR_SHAPE, "N=%d must be a multiple of 8 in [8, %d]", N, W4A8_MAX_N);
+  if (T > 0 && (!row_of_slot_dev || !weights_dev || !out_bf16_dev || (R > 0 && !C_bf16_dev)))
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(C_bf16_dev, 16) || !aligned(out_bf16_dev, 16) || !aligned(row_of_slot_dev, 4) ||
+      !aligned(weights_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "C and out need 16-byte, row_of_slot and weights 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  int st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  if (T == 0) return ok();
+  hipError_t e = w4a8::launch_combine(C_bf16_dev, R, N, row_of_slot_dev, weights_dev, T, top_k, out_bf16_dev,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -113,6 +113,17 @@ def test_quantize_gather_host_validation(lib):
     assert lib.w4a8_last_error() != b""
 
 
+def test_combine_host_validation(lib):
+    c = lib.w4a8_combine
+    assert c(P16, 8, 64, P16, P16, 4, 0, P16, NUL) == 2      # top_k = 0
+    assert c(P16, 8, 60, P16, P16, 4, 2, P16, NUL) == 2      # N % 8
+    assert c(P16, -1, 64, P16, P16, 4, 2, P16, NUL) == 2     # R < 0
+    assert c(P16, 8, 64, NUL, P16, 4, 2, P16, NUL) == 1      # null row map
+    assert c(P16, 8, 64, P16, P16, 4, 2, NUL, NUL) == 1      # null out
+    assert c(P4, 8, 64, P16, P16, 4, 2, P16, NUL) == 4       # misaligned C
+    assert lib.w4a8_last_error() != b""
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():
