@@ -32,15 +32,28 @@ combine_kernel(const uint16_t* __restrict__ C, int R, int N, const int32_t* __re
   const float* ws = weights + (size_t)t * top_k;
   for (int c0 = threadIdx.x * 8; c0 < N; c0 += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < top_k; ++j) {
-      const int r = rs[j];
-      if (r < 0 || r >= R) continue;  // a slot that names no row
-      const float w = ws[j];
-      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(C + (size_t)r * N + c0));
+    // eight slots' loads in flight at once, then their terms in slot order
+    for (int j0 = 0; j0 < top_k; j0 += 8) {
+      v4u v[8];
+      float wv[8];
+      bool ok[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = acc[2 * i] + w * __uint_as_float(v[i] << 16);
-        acc[2 * i + 1] = acc[2 * i + 1] + w * __uint_as_float(v[i] & 0xffff0000u);
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const int r = j < top_k ? rs[j] : -1;
+        ok[u] = r >= 0 && r < R;  // a slot that names no row contributes nothing
+        wv[u] = ok[u] ? ws[j] : 0.f;
+        v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(C + (size_t)r * N + c0))
+                     : v4u{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = acc[2 * i] + wv[u] * __uint_as_float(v[u][i] << 16);
+          acc[2 * i + 1] = acc[2 * i + 1] + wv[u] * __uint_as_float(v[u][i] & 0xffff0000u);
+        }
       }
     }
     v4u o;
