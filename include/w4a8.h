@@ -168,6 +168,28 @@ int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of
                  const float* weights_dev, int T, int top_k, uint16_t* out_bf16_dev, void* stream);
 
 /*
+ * w4a8_swiglu_quant -- the step between the two projections (humming PR
+ * #129 and PR #58 benchmark gate/up and down as a pair): SwiGLU of the
+ * gate/up output, requantized to E4M3 with one fp32 scale per (row, 128) for
+ * the down projection's A and a_scales.
+ *
+ * C_bf16_dev    uint16 (bf16 bits) [R][2I]: gate in columns 0 .. I-1, up in
+ *               columns I .. 2I-1.  16-byte aligned.
+ * A_fp8_dev     out uint8 [R][I] E4M3FN codes.  16-byte aligned.
+ * a_scales_dev  out fp32 per (row, 128-column group) in a_scale_layout
+ *               (row-major [R][I/128] or M-major [I/128][R]).  4-byte aligned.
+ * h = silu(g) * u = (g / (1 + e^-g)) * u in fp32 by a fixed sequence of IEEE
+ * single operations (e^x: Cody and Waite's two-constant reduction with
+ * ln2 = 0.693359375 + (ln2 - 0.693359375), a degree-7 Taylor polynomial by
+ * Horner's rule, exact scaling by 2^n; x clamped to [-88, 89]; no fused
+ * multiply-add), then per group s = amax|h| / 448 (1 if all zero) and the
+ * E4M3FN code of clip(h / s, +-448), round to nearest even, sign kept.
+ * Limits: R >= 0, I % 128 == 0, 128 <= I <= W4A8_MAX_K.  R == 0 does nothing.
+ */
+int w4a8_swiglu_quant(const uint16_t* C_bf16_dev, int R, int I, uint8_t* A_fp8_dev, float* a_scales_dev,
+                      int a_scale_layout, void* stream);
+
+/*
  * w4a8_grouped_gemm -- the grouped W4A8 GEMM.
  *
  * A_fp8_dev          uint8 [R][K] E4M3 codes; rows offsets[e]..offsets[e+1]-1

@@ -11,6 +11,7 @@ torch when the caller does not pass them.
     grouped_gemm(A, SA, layout, B, SB, expert_offsets, out=None) -> C (bf16)
     quantize_gather(x, row_of_slot, top_k, R, layout) -> A (E4M3 codes), SA
     combine(C, row_of_slot, weights, top_k, out=None) -> per-token bf16 sums
+    swiglu_quant(C, layout) -> A (E4M3 codes of silu(gate) * up), SA
 """
 
 from ._lib import (  # noqa: F401
@@ -26,4 +27,5 @@ from ._lib import (  # noqa: F401
     plan_params,
     quantize_gather,
     route_prep,
+    swiglu_quant,
 )

@@ -40,6 +40,8 @@ def _declare(lib):
     lib.w4a8_plan.restype = i32
     lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_swiglu_quant.argtypes = [vp, i32, i32, vp, vp, i32, vp]
+    lib.w4a8_swiglu_quant.restype = i32
     lib.w4a8_combine.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp]
     lib.w4a8_combine.restype = i32
     lib.w4a8_quantize_gather.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, i32, vp]
@@ -233,3 +235,24 @@ def combine(C: torch.Tensor, row_of_slot: torch.Tensor, weights: torch.Tensor, t
     _check("w4a8_combine", lib.w4a8_combine(_ptr(C), R, N, _ptr(row_of_slot), _ptr(weights), T, int(top_k),
                                             _ptr(out), _stream()))
     return out
+
+
+def swiglu_quant(C: torch.Tensor, layout: int, A: Optional[torch.Tensor] = None, SA: Optional[torch.Tensor] = None):
+    """Gate/up output C [R, 2I] (bf16; gate columns first) -> (A uint8 [R, I]
+    E4M3 codes of silu(gate) * up, SA fp32 scales [R, I/128] for layout 0 or
+    [I/128, R] for layout 1)."""
+    lib = load()
+    if C.dim() != 2 or C.shape[1] % 2:
+        raise ValueError("C must be [R, 2I]")
+    R, I = C.shape[0], C.shape[1] // 2
+    if C.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("C must be bfloat16 (or 16-bit integer bits)")
+    _need(C, "C", C.dtype)
+    if A is None:
+        A = torch.empty((R, I), dtype=torch.uint8, device=C.device)
+    if SA is None:
+        SA = torch.empty((R, I // 128) if layout == 0 else (I // 128, R), dtype=torch.float32, device=C.device)
+    _need(A, "A", torch.uint8, R * I)
+    _need(SA, "a_scales", torch.float32, R * (I // 128))
+    _check("w4a8_swiglu_quant", lib.w4a8_swiglu_quant(_ptr(C), R, I, _ptr(A), _ptr(SA), int(layout), _stream()))
+    return A, SA

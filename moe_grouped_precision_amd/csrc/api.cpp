@@ -221,4 +221,24 @@ int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of
   return ok();
 }
 
+int w4a8_swiglu_quant(const uint16_t* C_bf16_dev, int R, int I, uint8_t* A_fp8_dev, float* a_scales_dev,
+                      int a_scale_layout, void* stream) {
+  if (R < 0) return fail(W4A8_ERR_SHAPE, "R=%d", R);
+  if (I < 128 || I % 128 || I > W4A8_MAX_K)
+    return fail(W4A8_ERR_SHAPE, "I=%d must be a multiple of 128 in [128, %d]", I, W4A8_MAX_K);
+  if (a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR)
+    return fail(W4A8_ERR_LAYOUT, "a_scale_layout=%d is neither row-major (0) nor M-major (1)", a_scale_layout);
+  if (R > 0 && (!C_bf16_dev || !A_fp8_dev || !a_scales_dev)) return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(C_bf16_dev, 16) || !aligned(A_fp8_dev, 16) || !aligned(a_scales_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "C and A need 16-byte, scales 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  int st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  if (R == 0) return ok();
+  hipError_t e = w4a8::launch_swiglu_quant(C_bf16_dev, R, I, A_fp8_dev, a_scales_dev, a_scale_layout,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "swiglu_quant launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

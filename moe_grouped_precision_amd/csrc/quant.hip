@@ -99,7 +99,93 @@ quant_gather_kernel(const uint16_t* __restrict__ x, int K, const int32_t* __rest
   }
 }
 
+// e^x by one fixed fp32 sequence, the same on both sides of the parity test:
+// Cody and Waite's two-constant reduction x = n ln2 + r (L_HI has 9
+// significant bits, so n * L_HI is exact for |n| <= 129), e^r by Horner's
+// rule on its Taylor polynomial to degree 7 (remainder below 2^-27 relative
+// for |r| <= ln2 / 2), exact scaling by 2^n.  x is clamped to [-88, 89]: at
+// the top the scaling overflows to inf, at the bottom e^x is far below 2^-24.
+// Separate rounded operations throughout (no fused multiply-add).
+constexpr float kLog2e = (float)1.4426950408889634;
+constexpr float kLnHi = 0.693359375f;
+constexpr float kLnLo = (float)(0.6931471805599453 - 0.693359375);
+__device__ __forceinline__ float exp_seq(float x) {
+#pragma clang fp contract(off)
+  x = fminf(fmaxf(x, -88.0f), 89.0f);
+  const float n = rintf(x * kLog2e);
+  const float r = (x - n * kLnHi) - n * kLnLo;
+  float p = (float)(1.0 / 5040.0);
+  p = p * r + (float)(1.0 / 720.0);
+  p = p * r + (float)(1.0 / 120.0);
+  p = p * r + (float)(1.0 / 24.0);
+  p = p * r + (float)(1.0 / 6.0);
+  p = p * r + (float)(1.0 / 2.0);
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, (int)n);
+}
+
+// SwiGLU of the gate/up output and its E4M3 requantization: one workgroup
+// per row; 8 lanes per 128-column group, 16 columns of gate (columns 0 ..
+// I-1) and the same 16 of up (columns I .. 2I-1) per lane; h = silu(g) * u =
+// (g / (1 + e^-g)) * u in fp32, then the quantization above.
+__global__ void __launch_bounds__(512)
+swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __restrict__ A, float* __restrict__ SA,
+                    int layout) {
+#pragma clang fp contract(off)
+  // M-major scales: consecutive rows on one XCD (see quant_gather_kernel)
+  const int r = (layout == 0 || (R & 7)) ? (int)blockIdx.x
+                                         : (int)((blockIdx.x & 7) * (R >> 3) + (blockIdx.x >> 3));
+  const int G = I >> 7;
+  const int lane8 = threadIdx.x & 7;
+  const int gsub = threadIdx.x >> 3;
+  const int gstep = blockDim.x >> 3;
+  const uint16_t* row = C + (size_t)r * 2 * I;
+  for (int g = gsub; g < G; g += gstep) {
+    const v4u* gp = reinterpret_cast<const v4u*>(row + g * 128 + lane8 * 16);
+    const v4u* up = reinterpret_cast<const v4u*>(row + I + g * 128 + lane8 * 16);
+    const v4u g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+    const v4u u0 = __builtin_nontemporal_load(up), u1 = __builtin_nontemporal_load(up + 1);
+    const uint32_t gw[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    const uint32_t uw[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+    float h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t gb = (i & 1) ? (gw[i >> 1] & 0xffff0000u) : (gw[i >> 1] << 16);
+      const uint32_t ub = (i & 1) ? (uw[i >> 1] & 0xffff0000u) : (uw[i >> 1] << 16);
+      const float gv = __uint_as_float(gb), uv = __uint_as_float(ub);
+      const float d = 1.0f + exp_seq(-gv);
+      h[i] = __fdiv_rn(gv, d) * uv;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(h[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 8));
+    m = fmaxf(m, __shfl_xor(m, 2, 8));
+    m = fmaxf(m, __shfl_xor(m, 4, 8));
+    const float s = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float y = fminf(fmaxf(__fdiv_rn(h[i], s), -448.0f), 448.0f);
+      c[i >> 2] |= e4m3_rne(y) << (8 * (i & 3));
+    }
+    const v4u out = {c[0], c[1], c[2], c[3]};
+    __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(A + (size_t)r * I + g * 128 + lane8 * 16));
+    if (lane8 == 0) SA[layout ? (size_t)g * R + r : (size_t)r * G + g] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_quant(const uint16_t* C, int R, int I, uint8_t* A, float* SA, int layout,
+                               hipStream_t stream) {
+  if (R == 0) return hipSuccess;
+  const int G = I >> 7;
+  const int threads = 8 * (G < 64 ? ((G + 7) & ~7) : 64);
+  hipLaunchKernelGGL(swiglu_quant_kernel, dim3(R), dim3(threads), 0, stream, C, R, I, A, SA, layout);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_gather(const uint16_t* x, int T, int K, const int32_t* row_of_slot, int top_k, int R,
                                uint8_t* A, float* SA, int layout, hipStream_t stream) {

@@ -25,6 +25,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t strea
 hipError_t grouped_gemm_occupancy(int* blocks);
 hipError_t launch_combine(const uint16_t* C, int R, int N, const int32_t* row_of_slot, const float* weights, int T,
                           int top_k, uint16_t* out, hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t* C, int R, int I, uint8_t* A, float* SA, int layout,
+                               hipStream_t stream);
 hipError_t launch_quant_gather(const uint16_t* x, int T, int K, const int32_t* row_of_slot, int top_k, int R,
                                uint8_t* A, float* SA, int layout, hipStream_t stream);
 

@@ -124,6 +124,16 @@ def test_combine_host_validation(lib):
     assert lib.w4a8_last_error() != b""
 
 
+def test_swiglu_quant_host_validation(lib):
+    f = lib.w4a8_swiglu_quant
+    assert f(P16, -1, 256, P16, P16, 0, NUL) == 2       # R < 0
+    assert f(P16, 8, 200, P16, P16, 0, NUL) == 2        # I % 128
+    assert f(P16, 8, 256, P16, P16, 2, NUL) == 3        # bad layout
+    assert f(NUL, 8, 256, P16, P16, 0, NUL) == 1        # null C
+    assert f(P4, 8, 256, P16, P16, 0, NUL) == 4         # misaligned C
+    assert lib.w4a8_last_error() != b""
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():
