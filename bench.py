@@ -217,6 +217,38 @@ def measure_combine(reps=20, warmup=3):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measure_swiglu_quant(reps=20, warmup=3):
+    """SwiGLU + E4M3 requantization (w4a8_swiglu_quant) on the large prefill
+    gate/up output: 131072 rows x (2 x 2048) bf16, M-major scales.  Median of
+    `reps` launches timed with HIP events; HBM roofline on the bytes it must
+    move."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+
+    R, I = 131072, 2048
+    g = torch.Generator(device="cuda").manual_seed(23)
+    C = (torch.randn((R, 2 * I), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    A = torch.empty((R, I), dtype=torch.uint8, device="cuda")
+    SA = torch.empty((I // 128, R), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        w4a8.swiglu_quant(C, 1, A=A, SA=SA)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        w4a8.swiglu_quant(C, 1, A=A, SA=SA)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in ev])
+    nbytes = R * 2 * I * 2 + R * I + 4 * R * (I // 128)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{R} rows x (2 x {I}) bf16 gate/up output, M-major scales",
+            "us_median": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,7 +261,7 @@ def main():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, HBM read bandwidth)")
     ap.add_argument("--no-quantize", action="store_true",
-                    help="skip the activation-quantizer and combine measurements")
+                    help="skip the quantizer, SwiGLU-requantization and combine measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
@@ -338,10 +370,11 @@ def main():
         roof["measured_peak"] = measured
         roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
-    quant = comb = None
+    quant = comb = swq = None
     if not args.no_quantize:
-        log("timing the activation quantizer with gather and the top-k combine")
+        log("timing the activation quantizer, SwiGLU requantization and the top-k combine")
         quant = measure_quantize_gather()
+        swq = measure_swiglu_quant()
         comb = measure_combine()
 
     cpu = None
@@ -379,6 +412,7 @@ def main():
         "roofline": roof,
         "probes": probes,
         "quantize_gather": quant,
+        "swiglu_quant": swq,
         "combine": comb,
         "cpu_baseline": cpu,
     }
