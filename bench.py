@@ -217,6 +217,43 @@ def measure_combine(reps=20, warmup=3):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measure_route_prep_wide(reps=20, warmup=3):
+    """The routing prep (w4a8_route_prep) on a wide shared expert pool: 6144
+    experts, 16384 tokens, top-8, uniform without replacement (the largest
+    pool MoonEP PR #38 times).  Median of `reps` launches timed with HIP
+    events on the launch stream.  Every workgroup reads all ids from L2, so
+    the kernel is bound by that latency, not by HBM; the HBM roofline on the
+    bytes it must move is reported for completeness."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    E, T, k = 6144, 16384, 8
+    ids = synth.make_wide_routing(T, E, k, seed=6144).to("cuda")
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    r = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        w4a8.route_prep(ids, E, c, o, r)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        w4a8.route_prep(ids, E, c, o, r)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in ev])
+    lds = torch.cuda.get_device_properties(0).shared_memory_per_block
+    nbytes = 8 * T * k + 8 * E + 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{T} tokens x top-{k} over {E} experts, uniform routing",
+            "us_median": round(ms * 1e3, 2), "ranking_waves": w4a8.route_prep_waves(E, lds),
+            "lds_limit_bytes": int(lds), "algorithmic_bytes": int(nbytes),
+            "roofline": {"bound": "latency (every workgroup reads all ids from L2)", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def measure_swiglu_quant(reps=20, warmup=3):
     """SwiGLU + E4M3 requantization (w4a8_swiglu_quant) on the large prefill
     gate/up output: 131072 rows x (2 x 2048) bf16, M-major scales.  Median of
@@ -261,7 +298,8 @@ def main():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, HBM read bandwidth)")
     ap.add_argument("--no-quantize", action="store_true",
-                    help="skip the quantizer, SwiGLU-requantization and combine measurements")
+                    help="skip the quantizer, SwiGLU-requantization, combine and wide-pool "
+                         "routing-prep measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
@@ -370,12 +408,14 @@ def main():
         roof["measured_peak"] = measured
         roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
-    quant = comb = swq = None
+    quant = comb = swq = wide = None
     if not args.no_quantize:
-        log("timing the activation quantizer, SwiGLU requantization and the top-k combine")
+        log("timing the activation quantizer, SwiGLU requantization, the top-k combine "
+            "and the routing prep over 6144 experts")
         quant = measure_quantize_gather()
         swq = measure_swiglu_quant()
         comb = measure_combine()
+        wide = measure_route_prep_wide()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -414,6 +454,7 @@ def main():
         "quantize_gather": quant,
         "swiglu_quant": swq,
         "combine": comb,
+        "route_prep_wide_pool": wide,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -65,7 +65,9 @@ enum {
 };
 
 /* Limits of this version. */
-#define W4A8_MAX_EXPERTS 1024
+#define W4A8_MAX_EXPERTS 1024        /* grouped GEMM: per-expert tables live in LDS */
+#define W4A8_MAX_PREP_EXPERTS 65536  /* route prep and plan; the route prep's LDS fit
+                                        may lower it on a device (W4A8_ERR_CAPACITY) */
 #define W4A8_MAX_K 1048576     /* keeps every in-tile byte offset within 32 bits */
 #define W4A8_MAX_N 16777216    /* keeps work-item counts within 32 bits */
 
@@ -81,7 +83,16 @@ enum {
  *                    of one expert keep the flat (token, slot) order (a stable
  *                    counting sort), so the result is unique.  -1 for an
  *                    ignored id.
- * Limits: 1 <= E <= W4A8_MAX_EXPERTS, 0 <= T, 1 <= top_k, T*top_k < 2^31.
+ * Limits: 1 <= E <= W4A8_MAX_PREP_EXPERTS, 0 <= T, 1 <= top_k,
+ * T*top_k < 2^31.  Large E (MoonEP PR #38, background section: shared expert
+ * pools of thousands of experts): a workgroup of 16 waves holds
+ * (W + 2) * E + 16 int32 of LDS, where W waves rank the slots of the
+ * workgroup's chunk, each with its own copy of per-expert counts; W is the
+ * largest of 16, 15, ..., 1 that fits the device's per-workgroup LDS (the
+ * fit of MoonEP PR #38, change section, applied to the ranking copies: the
+ * other waves need no LDS, so the workgroup keeps all 16).  When not even
+ * one copy fits (E above 13648 on a 160 KB device) the call returns
+ * W4A8_ERR_CAPACITY before any launch.  The result does not depend on W.
  * Alignment: 4 bytes for every pointer.
  */
 int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E,
@@ -89,9 +100,19 @@ int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E,
                     int32_t* row_of_slot_dev, void* stream);
 
 /*
+ * w4a8_route_prep_waves -- host only, no device work: the ranking waves per
+ * workgroup w4a8_route_prep uses for E experts on a device whose workgroups
+ * may hold lds_limit_bytes of LDS (the largest W in 16..1 with
+ * 4 * ((W + 2) * E + 16) <= lds_limit_bytes).  Returns 0 when no W fits (the
+ * route prep then returns W4A8_ERR_CAPACITY) or E is outside
+ * [1, W4A8_MAX_PREP_EXPERTS].
+ */
+int w4a8_route_prep_waves(int E, size_t lds_limit_bytes);
+
+/*
  * w4a8_plan_bytes -- bytes a plan buffer needs for E experts and at most
  * max_total_rows routed rows (host only; no device work).  Returns 0 for
- * E outside [1, W4A8_MAX_EXPERTS] or a negative row count.
+ * E outside [1, W4A8_MAX_PREP_EXPERTS] or a negative row count.
  */
 size_t w4a8_plan_bytes(int E, int64_t max_total_rows);
 
@@ -111,9 +132,10 @@ size_t w4a8_plan_bytes(int E, int64_t max_total_rows);
  * Rule for an expert with rows r (integer only; constants by w4a8_plan_params):
  *   r == 0 -> no tile; r <= S_MAX -> one streaming tile, tile_m = ceil16(r);
  *   r > S_MAX -> n = ceil(r / T_MAX) MFMA tiles, tile_m = ceil16(ceil(r / n)).
- * Limits: as w4a8_grouped_gemm.  plan_bytes must hold at least the header
- * (W4A8_ERR_CAPACITY otherwise); a plan with more tiles than fit sets status 2
- * and writes the tiles that fit.  Alignment: 4 bytes.
+ * Limits: 1 <= E <= W4A8_MAX_PREP_EXPERTS (offsets are read from global
+ * memory, no LDS bound); N and K as w4a8_grouped_gemm.  plan_bytes must hold
+ * at least the header (W4A8_ERR_CAPACITY otherwise); a plan with more tiles
+ * than fit sets status 2 and writes the tiles that fit.  Alignment: 4 bytes.
  */
 int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K,
               void* plan_dev, size_t plan_bytes, void* stream);

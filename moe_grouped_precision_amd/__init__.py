@@ -7,6 +7,7 @@ computation runs in the library's HIP kernels.  Outputs are allocated with
 torch when the caller does not pass them.
 
     route_prep(topk_ids, E)          -> counts, expert_offsets, row_of_slot
+    route_prep_waves(E, lds_bytes)   -> waves per workgroup of the route prep (host only)
     plan(expert_offsets, E, N, K)    -> int32 plan (header + tiles)
     grouped_gemm(A, SA, layout, B, SB, expert_offsets, out=None) -> C (bf16)
     quantize_gather(x, row_of_slot, top_k, R, layout) -> A (E4M3 codes), SA
@@ -27,5 +28,6 @@ from ._lib import (  # noqa: F401
     plan_params,
     quantize_gather,
     route_prep,
+    route_prep_waves,
     swiglu_quant,
 )

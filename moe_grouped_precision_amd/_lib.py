@@ -34,6 +34,8 @@ def _declare(lib):
     i32, i64, sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
     lib.w4a8_route_prep.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
     lib.w4a8_route_prep.restype = i32
+    lib.w4a8_route_prep_waves.argtypes = [i32, sz]
+    lib.w4a8_route_prep_waves.restype = i32
     lib.w4a8_plan_bytes.argtypes = [i32, i64]
     lib.w4a8_plan_bytes.restype = sz
     lib.w4a8_plan.argtypes = [vp, i32, i32, i32, vp, sz, vp]
@@ -110,6 +112,11 @@ def plan_params():
 
 def plan_bytes(E: int, max_total_rows: int) -> int:
     return int(load(require_device=False).w4a8_plan_bytes(E, max_total_rows))
+
+
+def route_prep_waves(E: int, lds_limit_bytes: int) -> int:
+    """Waves per workgroup the route prep uses for E experts under an LDS limit (0: none fits)."""
+    return int(load(require_device=False).w4a8_route_prep_waves(E, lds_limit_bytes))
 
 
 def route_prep(topk_ids: torch.Tensor, E: int, counts=None, offsets=None, row_of_slot=None):

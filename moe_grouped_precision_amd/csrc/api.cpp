@@ -34,6 +34,7 @@ struct DeviceInfo {
   bool supported = false;
   int cus = 0;
   int grid = 0;  // workgroups of the persistent GEMM launch (one per CU)
+  size_t lds_limit = 0;  // LDS bytes one workgroup may hold
 };
 
 constexpr int kMaxDevices = 64;
@@ -54,6 +55,7 @@ int device_info(const DeviceInfo** out) {
     if (e != hipSuccess) return fail(W4A8_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     d.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
+    d.lds_limit = prop.sharedMemPerBlock;
     if (d.supported) {
       int blocks = 0;
       e = w4a8::grouped_gemm_occupancy(&blocks);
@@ -69,8 +71,8 @@ int device_info(const DeviceInfo** out) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_gemm_shape(int E, int N, int K) {
-  if (E < 1 || E > W4A8_MAX_EXPERTS) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_EXPERTS);
+int check_gemm_shape(int E, int N, int K, int max_experts = W4A8_MAX_EXPERTS) {
+  if (E < 1 || E > max_experts) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, max_experts);
   if (K < 128 || K % 128 || K > W4A8_MAX_K)
     return fail(W4A8_ERR_SHAPE, "K=%d must be a multiple of 128 in [128, %d]", K, W4A8_MAX_K);
   if (N < 32 || N % 32 || N > W4A8_MAX_N)
@@ -107,16 +109,22 @@ int w4a8_plan_params(int32_t* out_host, int n) {
 }
 
 size_t w4a8_plan_bytes(int E, int64_t max_total_rows) {
-  if (E < 1 || E > W4A8_MAX_EXPERTS || max_total_rows < 0) return 0;
+  if (E < 1 || E > W4A8_MAX_PREP_EXPERTS || max_total_rows < 0) return 0;
   // every expert contributes at most floor(rows/T_MAX) + 1 tiles, and only
   // experts with rows contribute
   int64_t tiles = max_total_rows / w4a8::T_MAX + (max_total_rows < E ? max_total_rows : E);
   return (size_t)(w4a8::PLAN_HEADER_WORDS + w4a8::PLAN_TILE_WORDS * tiles) * sizeof(int32_t);
 }
 
+int w4a8_route_prep_waves(int E, size_t lds_limit_bytes) {
+  if (E < 1 || E > W4A8_MAX_PREP_EXPERTS) return 0;
+  return w4a8::route_prep_waves(E, lds_limit_bytes);
+}
+
 int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E, int32_t* counts_dev,
                     int32_t* expert_offsets_dev, int32_t* row_of_slot_dev, void* stream) {
-  if (E < 1 || E > W4A8_MAX_EXPERTS) return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_EXPERTS);
+  if (E < 1 || E > W4A8_MAX_PREP_EXPERTS)
+    return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_PREP_EXPERTS);
   if (T < 0 || top_k < 1) return fail(W4A8_ERR_SHAPE, "T=%d top_k=%d", T, top_k);
   if ((int64_t)T * top_k >= (int64_t)1 << 31) return fail(W4A8_ERR_SHAPE, "T*top_k too large");
   const int n = T * top_k;
@@ -128,7 +136,11 @@ int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E, int32_
   const DeviceInfo* d = nullptr;
   int st = device_info(&d);
   if (st != W4A8_OK) return st;
-  hipError_t e = w4a8::launch_route_prep(topk_ids_dev, n, E, counts_dev, expert_offsets_dev,
+  const int waves = w4a8::route_prep_waves(E, d->lds_limit);
+  if (waves == 0)
+    return fail(W4A8_ERR_CAPACITY, "E=%d needs %zu bytes of LDS with one wave; the device allows %zu", E,
+                w4a8::route_prep_lds_bytes(E, 1), d->lds_limit);
+  hipError_t e = w4a8::launch_route_prep(topk_ids_dev, n, E, waves, counts_dev, expert_offsets_dev,
                                           row_of_slot_dev, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "route_prep launch: %s", hipGetErrorString(e));
   return ok();
@@ -136,7 +148,8 @@ int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E, int32_
 
 int w4a8_plan(const int32_t* expert_offsets_dev, int E, int N, int K, void* plan_dev,
               size_t plan_bytes, void* stream) {
-  int st = check_gemm_shape(E, N, K);
+  // the plan serves every E the route prep serves; N and K as for the GEMM
+  int st = check_gemm_shape(E, N, K, W4A8_MAX_PREP_EXPERTS);
   if (st != W4A8_OK) return st;
   if (!expert_offsets_dev || !plan_dev) return fail(W4A8_ERR_NULL, "null pointer argument");
   if (!aligned(expert_offsets_dev, 4) || !aligned(plan_dev, 4))

@@ -9,55 +9,86 @@
 // shared memory), re-laid for 64-wide waves.  Ranks inside an expert come
 // from wave ballots in flat slot order, never from atomic order, so the row
 // map is unique (MoonEP PR #38, correctness section, requires exact equality
-// with an independent reference).
+// with an independent reference).  The LDS need grows with W * E, so the
+// host picks the number of waves W to fit the device's per-workgroup LDS
+// (MoonEP PR #38, change section: drop one wave at a time from the largest
+// workgroup, report resource overflow when even one wave does not fit), which
+// carries the prep to thousands of experts.
 #include "w4a8_device.h"
 #include "w4a8_launch.h"
 
 namespace w4a8 {
 
-// B workgroups of W waves; workgroup b owns the contiguous slots
-// [b*chunk, (b+1)*chunk) and writes their rows.  Every workgroup histograms
+// B workgroups of ROUTE_MAX_WAVES waves; workgroup b owns the contiguous
+// slots [b*chunk, (b+1)*chunk) and writes their rows.  The first wr waves
+// rank (each one span of the chunk, with its own copy of the chunk's
+// counts); all waves histogram and scan.  Every workgroup histograms
 // all n ids (the slots before its chunk, its own chunk per wave, the slots
 // after it), so it knows each expert's offset and how many of the expert's
 // slots precede its chunk without any exchange between workgroups; workgroup
 // 0 also writes counts and offsets.  Reading all ids in every workgroup costs
 // L2 bandwidth only (the ids of a 16384-token batch are 512 KB), and the
-// result does not depend on the number of workgroups.
-// Dynamic LDS: own[W*E] + bef[W*E] + aft[W*E] + s_tot[E] + s_wave[16].
-__global__ void __launch_bounds__(1024)
-route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int chunk,
+// result does not depend on the number of workgroups or waves.
+// Dynamic LDS: own[wr*E] + bef[E] + aft[E] + s_wave[16] ints
+// (route_prep_lds_bytes); aft holds each expert's total once the counts are
+// summed.  Only a ranking wave needs its own copy of the chunk's counts; one
+// copy of the outside counts serves all waves, since LDS atomics serialize
+// only on equal addresses within one instruction.  So the LDS bounds the
+// number of ranking waves, never the workgroup's size.
+__global__ void __launch_bounds__(ROUTE_MAX_WAVES * 64)
+route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int chunk, int wr,
                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                   int32_t* __restrict__ row_of_slot) {
   extern __shared__ int smem[];
-  const int W = blockDim.x >> 6;
-  int* own = smem;                // [W][E]: chunk counts per wave, then running row per (wave, expert)
-  int* bef = smem + W * E;        // [W][E]: ids before the chunk
-  int* aft = bef + W * E;         // [W][E]: ids after the chunk
-  int* s_tot = aft + W * E;       // [E]
-  int* s_wave = s_tot + E;        // [16]
+  const int W = wr;               // ranking waves
+  int* own = smem;                // [W][E]: chunk counts per ranking wave, then running row per (wave, expert)
+  int* bef = smem + W * E;        // [E]: ids before the chunk
+  int* aft = bef + E;             // [E]: ids after the chunk; then the totals
+  int* s_wave = aft + E;          // [16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  for (int i = tid; i < 3 * W * E; i += blockDim.x) smem[i] = 0;
+  for (int i = tid; i < (W + 2) * E; i += blockDim.x) smem[i] = 0;
   __syncthreads();
 
   const int cbegin = min(n, (int)blockIdx.x * chunk);
   const int cend = min(n, cbegin + chunk);
-  // each wave owns one contiguous span of the chunk, a multiple of 64 long
+  // each ranking wave owns one contiguous span of the chunk, a multiple of
+  // 64 long; the other waves own none
   const int span = (((cend - cbegin + W - 1) / W) + 63) & ~63;
-  const int begin = min(cend, cbegin + wave * span);
-  const int end = min(cend, begin + span);
+  const int begin = wave < W ? min(cend, cbegin + wave * span) : cend;
+  const int end = wave < W ? min(cend, begin + span) : cend;
 
-  // phase 1: histograms (the order of the LDS atomics does not matter)
-  for (int i = tid; i < cbegin; i += blockDim.x) {
-    const int id = ids[i];
-    if (id >= 0 && id < E) atomicAdd(&bef[wave * E + id], 1);
+  // phase 1: histograms (the order of the LDS atomics does not matter).  The
+  // ids outside the chunk are read 16 bytes per lane with ROUTE_LOADS loads in
+  // flight (a workgroup of few waves would otherwise wait on one load at a
+  // time) and counted by position; the chunk's own ids per wave span.
+  auto count_outside = [&](unsigned i, int id) {
+    if (id >= 0 && id < E && (i < (unsigned)cbegin || i >= (unsigned)cend))
+      atomicAdd(&(i < (unsigned)cbegin ? bef : aft)[id], 1);
+  };
+  const int head = min(n, (int)((4 - ((reinterpret_cast<uintptr_t>(ids) >> 2) & 3)) & 3));
+  if (tid < head) count_outside(tid, ids[tid]);
+  const int nv = (n - head) >> 2;  // whole 16-byte units from ids + head
+  const int4* vec = reinterpret_cast<const int4*>(ids + head);
+  for (int u0 = tid; u0 < nv; u0 += ROUTE_LOADS * blockDim.x) {
+    int4 q[ROUTE_LOADS];
+#pragma unroll
+    for (int j = 0; j < ROUTE_LOADS; ++j) {
+      const int u = u0 + j * blockDim.x;
+      q[j] = u < nv ? vec[u] : make_int4(-1, -1, -1, -1);
+    }
+#pragma unroll
+    for (int j = 0; j < ROUTE_LOADS; ++j) {
+      const unsigned i = (unsigned)head + 4u * (unsigned)(u0 + j * blockDim.x);
+      count_outside(i, q[j].x);
+      count_outside(i + 1, q[j].y);
+      count_outside(i + 2, q[j].z);
+      count_outside(i + 3, q[j].w);
+    }
   }
-  for (int i = cend + tid; i < n; i += blockDim.x) {
-    const int id = ids[i];
-    if (id >= 0 && id < E) atomicAdd(&aft[wave * E + id], 1);
-  }
+  for (int i = head + 4 * nv + tid; i < n; i += blockDim.x) count_outside(i, ids[i]);
   for (int i = begin + lane; i < end; i += 64) {
     const int id = ids[i];
     if (id >= 0 && id < E) atomicAdd(&own[wave * E + id], 1);
@@ -72,19 +103,15 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
   for (int j = 0; j < per; ++j) {
     const int e = e0 + j;
     if (e < E) {
-      int before = 0, after = 0;
-      for (int w = 0; w < W; ++w) {
-        before += bef[w * E + e];
-        after += aft[w * E + e];
-      }
-      int run = before;
+      const int after = aft[e];
+      int run = bef[e];
       for (int w = 0; w < W; ++w) {
         const int c = own[w * E + e];
         own[w * E + e] = run;
         run += c;
       }
       const int tot = run + after;
-      s_tot[e] = tot;
+      aft[e] = tot;  // only this thread reads or writes column e
       if (blockIdx.x == 0) counts[e] = tot;
       local += tot;
     }
@@ -96,7 +123,7 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
     if (e < E) {
       if (blockIdx.x == 0) offsets[e] = ex;
       for (int w = 0; w < W; ++w) own[w * E + e] += ex;
-      ex += s_tot[e];
+      ex += aft[e];
     }
   }
   if (tid == 0 && blockIdx.x == 0) offsets[E] = total;
@@ -128,11 +155,11 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
 __global__ void __launch_bounds__(256)
 plan_kernel(const int32_t* __restrict__ offsets, int E, int N, int32_t* __restrict__ plan,
             int max_tiles) {
-  __shared__ int s_off[MAX_EXPERTS + 1];
+  // offsets are read from global memory (a few reads per expert, cached), so
+  // the plan has no LDS bound on E
+  const int32_t* s_off = offsets;
   __shared__ int s_wave[16];
   const int tid = threadIdx.x;
-  for (int i = tid; i <= E; i += blockDim.x) s_off[i] = offsets[i];
-  __syncthreads();
   int bad = 0;
   for (int i = tid; i < E; i += blockDim.x) bad |= (s_off[i + 1] < s_off[i]);
   if (tid == 0) bad |= (s_off[0] != 0);
@@ -191,12 +218,18 @@ plan_kernel(const int32_t* __restrict__ offsets, int E, int N, int32_t* __restri
   }
 }
 
-hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts,
+size_t route_prep_lds_bytes(int E, int waves) {
+  return ((size_t)(waves + 2) * E + 16) * sizeof(int);
+}
+
+int route_prep_waves(int E, size_t lds_limit) {
+  for (int w = ROUTE_MAX_WAVES; w >= 1; --w)
+    if (route_prep_lds_bytes(E, w) <= lds_limit) return w;
+  return 0;
+}
+
+hipError_t launch_route_prep(const int32_t* ids, int n, int E, int W, int32_t* counts,
                              int32_t* offsets, int32_t* row_of_slot, hipStream_t stream) {
-  // three [W][E] histograms in at most 48 KB of LDS
-  int W = 4096 / E;
-  if (W > 16) W = 16;
-  if (W < 1) W = 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   // chunks of at least 2048 slots (a multiple of 64), at most 256 workgroups
@@ -204,9 +237,8 @@ hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts,
   int chunk = kMinChunk;
   if ((n + chunk - 1) / chunk > kMaxBlocks) chunk = ((n + kMaxBlocks - 1) / kMaxBlocks + 63) & ~63;
   const int blocks = n > 0 ? (n + chunk - 1) / chunk : 1;
-  size_t lds = (size_t)(3 * W * E + E + 16) * sizeof(int);
-  hipLaunchKernelGGL(route_prep_kernel, dim3(blocks), dim3(W * 64), lds, stream, ids, n, E, nbits, chunk,
-                     counts, offsets, row_of_slot);
+  hipLaunchKernelGGL(route_prep_kernel, dim3(blocks), dim3(ROUTE_MAX_WAVES * 64), route_prep_lds_bytes(E, W),
+                     stream, ids, n, E, nbits, chunk, W, counts, offsets, row_of_slot);
   return hipGetLastError();
 }
 

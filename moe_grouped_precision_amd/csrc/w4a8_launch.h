@@ -17,7 +17,15 @@ struct GemmArgs {
   int E, N, K, layout;     // layout 0 row-major, 1 M-major
 };
 
-hipError_t launch_route_prep(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets,
+// Route prep: the workgroup holds ROUTE_MAX_WAVES waves, W of which rank
+// (1..ROUTE_MAX_WAVES), and route_prep_lds_bytes(E, W) bytes of LDS;
+// route_prep_waves picks the largest W that fits lds_limit bytes, 0 if none
+// does.
+constexpr int ROUTE_MAX_WAVES = 16;
+constexpr int ROUTE_LOADS = 16;  // 16-byte id loads in flight per lane
+size_t route_prep_lds_bytes(int E, int waves);
+int route_prep_waves(int E, size_t lds_limit);
+hipError_t launch_route_prep(const int32_t* ids, int n, int E, int W, int32_t* counts, int32_t* offsets,
                              int32_t* row_of_slot, hipStream_t stream);
 hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int max_tiles,
                        hipStream_t stream);

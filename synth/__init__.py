@@ -13,6 +13,7 @@ from .generate import (  # noqa: F401
     Problem,
     make_problem,
     make_routing,
+    make_wide_routing,
     quantize_fp8_rows,
     quantize_mxfp4,
     random_codes_problem,

@@ -80,6 +80,31 @@ def make_routing(kind: str, T: int, E: int, top_k: int, seed: int) -> torch.Tens
     return order[:, :top_k].to(torch.int32).contiguous()
 
 
+def make_wide_routing(T: int, E: int, top_k: int, seed: int, skew: bool = False) -> torch.Tensor:
+    """Top-k expert ids, int32 [T, top_k], for a wide expert pool (thousands
+    of experts, as in MoonEP PR #38's shared expert pools).  Distinct within a
+    token.  Uniform: the top-k of uniform random keys.  Skewed: expert weights
+    exp(9 u) (u uniform, so sizes span about four orders) sampled without
+    replacement by the Gumbel top-k rule.  Drawn in slices of 256 tokens to
+    keep the key matrix small."""
+    if not (1 <= top_k <= E):
+        raise ValueError("need 1 <= top_k <= E")
+    g = _gen(seed, _S_ROUTE)
+    logw = None
+    if skew:
+        logw = 9.0 * torch.rand((E,), generator=g, dtype=torch.float64)
+    out = []
+    for t0 in range(0, T, 256):
+        rows = min(256, T - t0)
+        keys = torch.rand((rows, E), generator=g, dtype=torch.float64)
+        if skew:
+            keys = logw - torch.log(-torch.log(keys.clamp_min(1e-300)))
+        out.append(torch.topk(keys, top_k, dim=1).indices.to(torch.int32))
+    if not out:
+        return torch.zeros((0, top_k), dtype=torch.int32)
+    return torch.cat(out).contiguous()
+
+
 def quantize_fp8_rows(x: torch.Tensor):
     """fp32 [R, K] -> (E4M3 codes uint8 [R, K], fp32 scales [R, K/128]).
 

@@ -54,7 +54,11 @@ def test_plan_bytes_bound(lib):
         off = np.concatenate([[0], np.cumsum(counts)])
         need = len(oracle.plan_ref(off, E, 256)) * 4
         assert w4a8.plan_bytes(E, int(off[-1])) >= need
-    assert w4a8.plan_bytes(0, 10) == 0 and w4a8.plan_bytes(1025, 10) == 0
+    for E in (2048, 8192, 65536):   # the plan serves the route prep's experts
+        counts = rng.integers(0, 40, size=E) * (rng.random(E) < 0.3)
+        off = np.concatenate([[0], np.cumsum(counts)])
+        assert w4a8.plan_bytes(E, int(off[-1])) >= len(oracle.plan_ref(off, E, 256)) * 4
+    assert w4a8.plan_bytes(0, 10) == 0 and w4a8.plan_bytes(65537, 10) == 0
     assert w4a8.plan_bytes(4, -1) == 0
     assert w4a8.plan_bytes(8, 0) == P.HEADER_WORDS * 4
 
@@ -97,6 +101,36 @@ def test_plan_and_route_host_validation(lib):
     assert lib.w4a8_route_prep(P16, -1, 2, 8, P16, P16, P16, NUL) == 2
     assert lib.w4a8_route_prep(P16, 4, 2, 8, NUL, P16, P16, NUL) == 1
     assert lib.w4a8_route_prep(ctypes.c_void_p((1 << 20) + 2), 4, 2, 8, P16, P16, P16, NUL) == 4
+    assert lib.w4a8_route_prep(P16, 4, 2, 65537, P16, P16, P16, NUL) == 2   # above the prep limit
+    assert lib.w4a8_plan(P16, 65537, 256, 512, P16, 1024, NUL) == 2
+    # the GEMM keeps its own, lower limit (per-expert tables in LDS)
+    assert lib.w4a8_grouped_gemm(P16, P16, 0, P16, P16, P16, 2048, 256, 512, P16, NUL) == 2
+
+
+LDS_160K = 160 * 1024
+
+
+def test_route_prep_waves_fit():
+    """The route prep's LDS fit (MoonEP PR #38, change section): the largest
+    wave count from 16 down whose LDS need, (W + 2) * E + 16 int32, fits the
+    device's per-workgroup LDS; none -> 0 (the call then reports
+    W4A8_ERR_CAPACITY)."""
+    def need(E, W):
+        return 4 * ((W + 2) * E + 16)
+    for E in list(range(1, 300)) + [341, 342, 1024, 2275, 2276, 2409, 2410, 4096, 8192, 13647, 13648, 13649]:
+        W = w4a8.route_prep_waves(E, LDS_160K)
+        if W:
+            assert 1 <= W <= 16 and need(E, W) <= LDS_160K
+            assert W == 16 or need(E, W + 1) > LDS_160K
+        else:
+            assert need(E, 1) > LDS_160K
+    assert w4a8.route_prep_waves(32, LDS_160K) == 16          # small E keeps the full workgroup
+    assert w4a8.route_prep_waves(1024, LDS_160K) == 16
+    assert w4a8.route_prep_waves(6144, LDS_160K) == 4
+    assert w4a8.route_prep_waves(13648, LDS_160K) == 1        # the largest E one wave serves
+    assert w4a8.route_prep_waves(13649, LDS_160K) == 0
+    assert w4a8.route_prep_waves(1024, 64 * 1024) == 13       # a 64 KB device
+    assert w4a8.route_prep_waves(0, LDS_160K) == 0 and w4a8.route_prep_waves(65537, 1 << 30) == 0
 
 
 def test_quantize_gather_host_validation(lib):

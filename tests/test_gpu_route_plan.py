@@ -85,3 +85,58 @@ def test_plan_boundaries_and_capacity(gpu_lib):
 def test_plan_bad_offsets(gpu_lib):
     _plan_case(gpu_lib, np.array([0, 10, 5, 20]), 3, 256)
     _plan_case(gpu_lib, np.array([3, 10, 15]), 2, 256)
+
+
+def _large_e_ids(T, top_k, E, seed, skew):
+    return synth.make_wide_routing(T, E, top_k, seed, skew)
+
+
+# The expert pools of MoonEP PR #38 (performance section: 1536 to 6144
+# experts with 123 to 16384 tokens), top-8, and the one-wave edge of a 160 KB
+# LDS workgroup (13648 experts).
+LARGE_E = [(1536, 123, False), (2048, 16384, False), (3072, 4096, True), (6144, 16384, False),
+           (6144, 123, True), (9216, 4096, True), (13648, 2048, False)]
+
+
+@pytest.mark.parametrize("E,T,skew", LARGE_E)
+def test_route_and_plan_large_e(gpu_lib, E, T, skew):
+    ids = _large_e_ids(T, 8, E, seed=E + T, skew=skew)
+    if E == 13648:
+        ids[::7, 3] = -1            # ignored ids at the edge too
+    off = _route_case(gpu_lib, ids, E)
+    _plan_case(gpu_lib, off, E, 4096, K=512)
+
+
+def test_route_large_e_capacity(gpu_lib):
+    # 65536 experts need 786 KB of LDS with a single wave: reported before any launch
+    ids = torch.zeros((4, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(gpu_lib.W4A8Error) as ei:
+        gpu_lib.route_prep(ids, 65536)
+    assert ei.value.status == 5
+
+
+def test_plan_largest_pool(gpu_lib):
+    # the plan has no LDS bound: 65536 experts, most of them empty
+    rng = np.random.default_rng(7)
+    E = 65536
+    counts = rng.integers(0, 300, size=E) * (rng.random(E) < 0.05)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    _plan_case(gpu_lib, off, E, 2048)
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("E,T,k", [(3072, 4096, 8), (32, 1, 2), (8, 3, 1), (6144, 123, 8)])
+def test_route_ids_not_16_byte_aligned(gpu_lib, shift, E, T, k):
+    # the histogram reads whole 16-byte units after a scalar head: ids that
+    # start 4, 8 or 12 bytes past a 16-byte boundary, short lists included
+    ids = _large_e_ids(T, k, E, seed=shift, skew=True)
+    buf = torch.full((T * k + 8,), -1, dtype=torch.int32, device="cuda")
+    buf[shift:shift + T * k] = ids.reshape(-1).cuda()
+    view = buf[shift:shift + T * k].view(T, k)
+    assert view.data_ptr() % 16 == 4 * shift
+    c, o, r = gpu_lib.route_prep(view, E)
+    torch.cuda.synchronize()
+    rc, ro, rr = route_ref(ids, E)
+    assert np.array_equal(c.cpu().numpy(), rc)
+    assert np.array_equal(o.cpu().numpy(), ro)
+    assert np.array_equal(r.cpu().numpy(), rr)

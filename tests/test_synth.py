@@ -65,3 +65,17 @@ def test_mxfp4_quantizer_rule():
     assert list(wd[1, 32:40]) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0]
     lut4 = e2m1_table()
     assert set(np.unique(np.abs(wd / np.repeat(scale, 32, axis=1)))) <= set(np.abs(lut4))
+
+
+def test_wide_routing_is_a_top_k_selection():
+    for skew in (False, True):
+        a = synth.make_wide_routing(300, 5000, 8, seed=3, skew=skew)
+        b = synth.make_wide_routing(300, 5000, 8, seed=3, skew=skew)
+        assert a.dtype == torch.int32 and a.shape == (300, 8) and torch.equal(a, b)
+        s = torch.sort(a, dim=1).values
+        assert bool((s[:, 1:] != s[:, :-1]).all()) and int(a.min()) >= 0 and int(a.max()) < 5000
+    assert synth.make_wide_routing(0, 64, 4, seed=1).shape == (0, 4)
+    # skew concentrates slots on heavy experts
+    u = torch.bincount(synth.make_wide_routing(2000, 2048, 8, 5).reshape(-1).long(), minlength=2048)
+    w = torch.bincount(synth.make_wide_routing(2000, 2048, 8, 5, skew=True).reshape(-1).long(), minlength=2048)
+    assert int(w.max()) > 4 * int(u.max())
