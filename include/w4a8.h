@@ -65,7 +65,7 @@ enum {
 };
 
 /* Limits of this version. */
-#define W4A8_MAX_EXPERTS 1024        /* grouped GEMM: per-expert tables live in LDS */
+#define W4A8_MAX_EXPERTS 2048        /* grouped GEMM: per-expert tables live in LDS */
 #define W4A8_MAX_PREP_EXPERTS 65536  /* route prep and plan; the route prep's LDS fit
                                         may lower it on a device (W4A8_ERR_CAPACITY) */
 #define W4A8_MAX_K 1048576     /* keeps every in-tile byte offset within 32 bits */

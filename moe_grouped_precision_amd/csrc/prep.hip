@@ -72,16 +72,23 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
   if (tid < head) count_outside(tid, ids[tid]);
   const int nv = (n - head) >> 2;  // whole 16-byte units from ids + head
   const int4* vec = reinterpret_cast<const int4*>(ids + head);
-  for (int u0 = tid; u0 < nv; u0 += ROUTE_LOADS * blockDim.x) {
+  // units [0, ub) reach before the chunk, units [ua, nv) after it; the loop
+  // runs over both ranges as one index space and skips the units inside
+  const int ub = min(nv, cbegin > head ? (cbegin - head + 3) >> 2 : 0);
+  const int ua = max(ub, min(nv, cend > head ? (cend - head) >> 2 : 0));
+  const int nvis = ub + (nv - ua);
+  auto unit = [&](int v) { return v < ub ? v : v - ub + ua; };
+  for (int v0 = tid; v0 < nvis; v0 += ROUTE_LOADS * blockDim.x) {
     int4 q[ROUTE_LOADS];
 #pragma unroll
     for (int j = 0; j < ROUTE_LOADS; ++j) {
-      const int u = u0 + j * blockDim.x;
-      q[j] = u < nv ? vec[u] : make_int4(-1, -1, -1, -1);
+      const int v = v0 + j * blockDim.x;
+      q[j] = v < nvis ? vec[unit(v)] : make_int4(-1, -1, -1, -1);
     }
 #pragma unroll
     for (int j = 0; j < ROUTE_LOADS; ++j) {
-      const unsigned i = (unsigned)head + 4u * (unsigned)(u0 + j * blockDim.x);
+      const int v = v0 + j * blockDim.x;
+      const unsigned i = (unsigned)head + 4u * (unsigned)(v < nvis ? unit(v) : 0);
       count_outside(i, q[j].x);
       count_outside(i + 1, q[j].y);
       count_outside(i + 2, q[j].z);

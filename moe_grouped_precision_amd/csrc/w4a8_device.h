@@ -36,7 +36,9 @@ constexpr int PLAN_OK = 0;
 constexpr int PLAN_BAD_OFFSETS = 1;
 constexpr int PLAN_CAPACITY = 2;
 
-constexpr int MAX_EXPERTS = 1024;
+// per-expert tables of the GEMM prologue live in LDS beside the staging
+// buffers: 2048 experts keep the total under 160 KB
+constexpr int MAX_EXPERTS = 2048;
 
 struct TileChoice {
   int cls;

@@ -77,7 +77,7 @@ NUL = ctypes.c_void_p(0)
 
 @pytest.mark.parametrize("args,status", [
     ((P16, P16, 0, P16, P16, P16, 0, 256, 512, P16, NUL), 2),      # E = 0
-    ((P16, P16, 0, P16, P16, P16, 1025, 256, 512, P16, NUL), 2),   # E too large
+    ((P16, P16, 0, P16, P16, P16, 2049, 256, 512, P16, NUL), 2),   # E too large
     ((P16, P16, 0, P16, P16, P16, 8, 256, 500, P16, NUL), 2),      # K % 128
     ((P16, P16, 0, P16, P16, P16, 8, 256, (1 << 20) + 128, P16, NUL), 2),  # K above the limit
     ((P16, P16, 0, P16, P16, P16, 8, 48, 512, P16, NUL), 2),       # N % 32
@@ -104,7 +104,7 @@ def test_plan_and_route_host_validation(lib):
     assert lib.w4a8_route_prep(P16, 4, 2, 65537, P16, P16, P16, NUL) == 2   # above the prep limit
     assert lib.w4a8_plan(P16, 65537, 256, 512, P16, 1024, NUL) == 2
     # the GEMM keeps its own, lower limit (per-expert tables in LDS)
-    assert lib.w4a8_grouped_gemm(P16, P16, 0, P16, P16, P16, 2048, 256, 512, P16, NUL) == 2
+    assert lib.w4a8_grouped_gemm(P16, P16, 0, P16, P16, P16, 4096, 256, 512, P16, NUL) == 2
 
 
 LDS_160K = 160 * 1024

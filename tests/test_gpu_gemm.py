@@ -212,3 +212,25 @@ def test_bad_offsets_write_nothing(gpu_lib):
     gpu_lib.grouped_gemm(A.cuda(), SA.cuda(), 0, B.cuda(), SB.cuda(), bad.cuda(), out=C)
     torch.cuda.synchronize()
     assert torch.all(C == 7.0)
+
+
+@pytest.mark.parametrize("E,T,skew,N", [(1536, 123, False, 256), (2048, 4096, True, 192), (2048, 16, False, 320)])
+def test_wide_expert_pool(gpu_lib, E, T, skew, N):
+    """The grouped GEMM over the wide shared pools of MoonEP PR #38
+    (performance section: 1536 and 2048 experts), rows from the GPU route
+    prep of top-8 wide routing: hundreds of one- to few-row streaming experts
+    and, skewed, MFMA-class experts beside them."""
+    ids = synth.make_wide_routing(T, E, 8, seed=E + T, skew=skew)
+    counts, off_ref, _ = route_ref(ids, E)
+    _, off_dev, _ = gpu_lib.route_prep(ids.cuda(), E)
+    assert np.array_equal(off_dev.cpu().numpy(), off_ref)
+    A, SA, B, SB, off = synth.random_codes_problem(counts.tolist(), N, 256, seed=E + N)
+    assert np.array_equal(off.numpy(), off_ref)
+    for layout in (0, 1):
+        SA_l = SA if layout == 0 else synth.to_m_major(SA)
+        C = _run(gpu_lib, A.cuda(), SA_l.cuda(), layout, B.cuda(), SB.cuda(), off_dev)
+        ref = grouped_gemm_bf16(A, SA_l.reshape(-1), layout, B, SB, off)
+        err = parity_error(bits_of(C), ref)
+        print(f"E={E} T={T} skew={skew} N={N} layout={layout} R={int(off[-1])} "
+              f"max_rows={int(counts.max())} parity_error={err:.3e}", flush=True)
+        assert err <= TOL
