@@ -288,12 +288,14 @@ struct StreamItem {
     // add the two K halves in LDS (nothing is in flight -- the last wait was
     // for zero -- and every wave is past its last LDS read after this barrier)
     __syncthreads();
-    v4f* red = reinterpret_cast<v4f*>(lds);
+    // one per-lane base (the wave's slice of the scratch is a uniform offset),
+    // constant offsets per (unit, row block)
+    v4f* red = reinterpret_cast<v4f*>(lds) + uniform(wn) * (NBW * MB * 64) + lane;
     if (kh == 1) {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < MB; ++i) red[((wn * NBW + j) * MB + i) * 64 + lane] = acc[j][i];
+        for (int i = 0; i < MB; ++i) red[(j * MB + i) * 64] = acc[j][i];
     }
     __syncthreads();
     if (kh == 0) {
@@ -305,7 +307,7 @@ struct StreamItem {
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
             const int n = n0 + (wn * NBW + j) * 16 + q * 4;
-            const v4f o = red[((wn * NBW + j) * MB + i) * 64 + lane];
+            const v4f o = red[(j * MB + i) * 64];
             if (n < N) store_bf16x4(crow + n, acc[j][i] + o);
           }
         }
