@@ -49,9 +49,6 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  for (int i = tid; i < (W + 2) * E; i += blockDim.x) smem[i] = 0;
-  __syncthreads();
-
   const int cbegin = min(n, (int)blockIdx.x * chunk);
   const int cend = min(n, cbegin + chunk);
   // each ranking wave owns one contiguous span of the chunk, a multiple of
@@ -59,6 +56,12 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
   const int span = (((cend - cbegin + W - 1) / W) + 63) & ~63;
   const int begin = wave < W ? min(cend, cbegin + wave * span) : cend;
   const int end = wave < W ? min(cend, begin + span) : cend;
+  // the first 64 ids of the span, loaded before the LDS is cleared and kept
+  // in a register for the ranks (a small batch is all first ids)
+  const int id_first = begin + lane < end ? ids[begin + lane] : -1;
+
+  for (int i = tid; i < (W + 2) * E; i += blockDim.x) smem[i] = 0;
+  __syncthreads();
 
   // phase 1: histograms (the order of the LDS atomics does not matter).  The
   // ids outside the chunk are read 16 bytes per lane with ROUTE_LOADS loads in
@@ -96,7 +99,8 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
     }
   }
   for (int i = head + 4 * nv + tid; i < n; i += blockDim.x) count_outside(i, ids[i]);
-  for (int i = begin + lane; i < end; i += 64) {
+  if (id_first >= 0 && id_first < E) atomicAdd(&own[wave * E + id_first], 1);
+  for (int i = begin + 64 + lane; i < end; i += 64) {
     const int id = ids[i];
     if (id >= 0 && id < E) atomicAdd(&own[wave * E + id], 1);
   }
@@ -141,7 +145,7 @@ route_prep_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits, int 
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int i0 = begin; i0 < end; i0 += 64) {
     const int i = i0 + lane;
-    const int id = (i < end) ? ids[i] : -1;
+    const int id = i0 == begin ? id_first : (i < end) ? ids[i] : -1;
     const bool valid = id >= 0 && id < E;
     uint64_t m = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
