@@ -254,6 +254,51 @@ def measure_route_prep_wide(reps=20, warmup=3):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measure_gemm_wide_pool(reps=5, warmup=2):
+    """The grouped GEMM over a 2048-expert pool (the 2048-expert shape of
+    MoonEP PR #38's performance table, 16384 tokens at top-8, uniform routing)
+    at the benchmark's gate/up expert shape N=4096, K=6144 (humming PR #129
+    "Results"), random codes drawn on the GPU.  Every expert gets rows, so
+    the 27 GB of weights are read once and the launch is HBM-bound (about
+    225 flop per byte, below the MFMA ridge).  Median of `reps` launches timed
+    with HIP events on the launch stream."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    E, T, k, N, K = 2048, 16384, 8, 4096, 6144
+    ids = synth.make_wide_routing(T, E, k, seed=2048).to("cuda")
+    counts, off, _ = w4a8.route_prep(ids, E)
+    counts = counts.cpu().numpy()
+    R = int(counts.sum())
+    A, SA, B, SB = synth.wide_pool_codes(counts.tolist(), N, K, seed=11)
+    C = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        w4a8.grouped_gemm(A, SA, 0, B, SB, off, out=C)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        w4a8.grouped_gemm(A, SA, 0, B, SB, off, out=C)
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.median([a.elapsed_time(b) for a, b in ev])
+    hit = int((counts > 0).sum())
+    nbytes = hit * N * K * (1 / 2 + 1 / 32) + R * K + R * (K // 128) * 4 + R * N * 2 + 4 * (E + 1)
+    flops = 2.0 * R * N * K
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"workload": f"{T} tokens x top-{k} over {E} experts ({hit} with rows, at most {int(counts.max())} rows), "
+                       f"N={N} K={K}, uniform routing, row-major scales",
+           "us_median": round(ms * 1e3, 1), "algorithmic_bytes": int(nbytes), "flop": flops,
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del A, SA, B, SB, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_swiglu_quant(reps=20, warmup=3):
     """SwiGLU + E4M3 requantization (w4a8_swiglu_quant) on the large prefill
     gate/up output: 131072 rows x (2 x 2048) bf16, M-major scales.  Median of
@@ -299,7 +344,7 @@ def main():
                     help="skip the measured-peak probes (MFMA rate, HBM read bandwidth)")
     ap.add_argument("--no-quantize", action="store_true",
                     help="skip the quantizer, SwiGLU-requantization, combine and wide-pool "
-                         "routing-prep measurements")
+                         "routing-prep and GEMM measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
     args = ap.parse_args()
@@ -408,14 +453,15 @@ def main():
         roof["measured_peak"] = measured
         roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
-    quant = comb = swq = wide = None
+    quant = comb = swq = wide = wide_gemm = None
     if not args.no_quantize:
-        log("timing the activation quantizer, SwiGLU requantization, the top-k combine "
-            "and the routing prep over 6144 experts")
+        log("timing the activation quantizer, SwiGLU requantization, the top-k combine, "
+            "the routing prep over 6144 experts and the GEMM over 2048 experts")
         quant = measure_quantize_gather()
         swq = measure_swiglu_quant()
         comb = measure_combine()
         wide = measure_route_prep_wide()
+        wide_gemm = measure_gemm_wide_pool()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -455,6 +501,7 @@ def main():
         "swiglu_quant": swq,
         "combine": comb,
         "route_prep_wide_pool": wide,
+        "grouped_gemm_wide_pool": wide_gemm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -18,4 +18,5 @@ from .generate import (  # noqa: F401
     quantize_mxfp4,
     random_codes_problem,
     to_m_major,
+    wide_pool_codes,
 )

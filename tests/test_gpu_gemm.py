@@ -234,3 +234,38 @@ def test_wide_expert_pool(gpu_lib, E, T, skew, N):
         print(f"E={E} T={T} skew={skew} N={N} layout={layout} R={int(off[-1])} "
               f"max_rows={int(counts.max())} parity_error={err:.3e}", flush=True)
         assert err <= TOL
+
+
+def test_wide_pool_full_size_sampled(gpu_lib):
+    """2048 experts at the benchmark's gate/up shape (N=4096, K=6144), 16384
+    tokens at top-8, rows from the GPU route prep: every one of the 2048
+    experts gets rows, most of them near the 64-row boundary between the two
+    classes.  The oracle recomputes sampled rows of 16 experts of both
+    classes (first, last and a random row each) on 512 sampled columns."""
+    E, T, k, N, K = 2048, 16384, 8, 4096, 6144
+    ids = synth.make_wide_routing(T, E, k, seed=2048)
+    counts, off, _ = route_ref(ids, E)
+    _, off_dev, _ = gpu_lib.route_prep(ids.cuda(), E)
+    assert np.array_equal(off_dev.cpu().numpy(), off)
+    A, SA, B, SB = synth.wide_pool_codes(counts.tolist(), N, K, seed=11)
+    C = _run(gpu_lib, A, SA, 0, B, SB, off_dev)
+    rng = np.random.default_rng(12)
+    stream_e = np.nonzero((counts > 0) & (counts <= 64))[0]
+    mfma_e = np.nonzero(counts > 64)[0]
+    experts = np.concatenate([rng.choice(stream_e, 8, replace=False), rng.choice(mfma_e, 8, replace=False)])
+    rows, ex = [], []
+    for j, e in enumerate(experts):
+        lo, hi = int(off[e]), int(off[e + 1])
+        for r in sorted({lo, hi - 1, int(rng.integers(lo, hi))}):
+            rows.append(r)
+            ex.append(j)
+    rows = np.array(rows, dtype=np.int64)
+    cols = np.unique(np.concatenate([[0, 63, 64, 511, 512, N - 1], rng.choice(N, 506, replace=False)]))
+    rows_t = torch.from_numpy(rows).cuda()
+    exp_t = torch.from_numpy(experts).cuda()
+    ref = bf16_rne_bits(rows_gemm_f64(A[rows_t].cpu().numpy(), SA[rows_t].cpu().numpy(), np.array(ex),
+                                      B[exp_t].cpu().numpy(), SB[exp_t].cpu().numpy(), cols=cols))
+    got = bits_of(C[rows_t][:, torch.from_numpy(cols).cuda()])
+    err = parity_error(got, ref)
+    print(f"wide pool E={E} rows={len(rows)} cols={len(cols)} classes 8+8 parity_error={err:.3e}", flush=True)
+    assert err <= TOL
