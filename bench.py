@@ -34,6 +34,10 @@ MFMA_FP8_PEAK_TFS = 5000.0  # MI355X dense FP8 MFMA, published (FP8 x FP4 runs a
 INFINITY_CACHE_BYTES = 256 << 20
 
 DEFAULT_STEPS = {"prefill_gateup": 20}
+# untimed steps before the timed region: enough continuous work (about 20 ms
+# on decode, 160 ms on the large prefill) for the GPU clocks to settle; with
+# 10 warmup steps the first ~10 ms of timed decode steps ran 8% slower
+DEFAULT_WARMUP = {"prefill_gateup": 50}
 BOUND = {"prefill_gateup": "mfma", "prefill_down": "mfma"}
 
 
@@ -335,7 +339,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="decode_gateup")
     ap.add_argument("--layout", type=int, default=None, help="0 row-major, 1 M-major input scales")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -367,6 +371,8 @@ def main():
     name = args.config
     cfg = synth.CONFIGS[name]
     steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(name, 50)
+    if args.warmup is None:
+        args.warmup = DEFAULT_WARMUP.get(name, 200)
     layout = args.layout if args.layout is not None else (1 if name == "prefill_gateup" else 0)
     w4a8.load()
     dev = torch.device("cuda:0")

@@ -107,8 +107,7 @@ def make_wide_routing(T: int, E: int, top_k: int, seed: int, skew: bool = False)
 
 def wide_pool_codes(counts, N: int, K: int, seed: int, device: str = "cuda"):
     """Raw random codes for a wide expert pool, drawn directly on `device`
-    one expert at a time (uint8 throughout, so a pool of tens of GB never
-    passes through a wider type).  ``counts`` rows per expert, laid out
+    as uint8 (a pool of tens of GB never passes through a wider type).  ``counts`` rows per expert, laid out
     contiguously in expert order.  A avoids the two E4M3 NaN codes, SA is
     U(0.01, 4) fp32 row-major, B any byte, SB uniform in [112, 132).
     Returns (A, SA, B, SB) on `device`."""
@@ -119,11 +118,8 @@ def wide_pool_codes(counts, N: int, K: int, seed: int, device: str = "cuda"):
     A = torch.randint(0, 256, (R, K), generator=g, dtype=torch.uint8, device=device)
     A[(A & 0x7F) == 0x7F] = 0x38
     SA = torch.rand((R, K // 128), generator=g, dtype=torch.float32, device=device) * 4 + 0.01
-    B = torch.empty((E, N, K // 2), dtype=torch.uint8, device=device)
-    SB = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device)
-    for e in range(E):
-        B[e] = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8, device=device)
-        SB[e] = torch.randint(112, 132, (N, K // 32), generator=g, dtype=torch.uint8, device=device)
+    B = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.uint8, device=device)
+    SB = torch.randint(112, 132, (E, N, K // 32), generator=g, dtype=torch.uint8, device=device)
     return A, SA, B, SB
 
 
