@@ -24,7 +24,8 @@ Modules:
   quant   -- bf16 tokens -> E4M3 codes with per-(row, 128) amax/448 scales,
              gathered to the grouped row of every slot.
   combine -- top-k weighted sum of grouped output rows back to tokens.
-  swiglu  -- silu(gate) * up of the gate/up output, requantized to E4M3.
+  swiglu  -- silu(gate) * up of the gate/up output, requantized to E4M3, in
+             fp64, and the admissibility check of an fp32 result against it.
 
 Parity status: no page prints a worked example or output value for any of
 these, so every function is pinned by closed forms, invariants, exact
@@ -45,4 +46,4 @@ from .plan import PLAN_PARAMS, plan_ref, tile_rule  # noqa: F401
 from .route import route_ref  # noqa: F401
 from .quant import bf16_bits_to_f32, e4m3_encode_rne, quantize_gather, quantize_tokens  # noqa: F401
 from .combine import combine_ref  # noqa: F401
-from .swiglu import exp_f32, swiglu_f32, swiglu_quant  # noqa: F401
+from .swiglu import check_swiglu_quant, silu_f64, swiglu_f64, swiglu_quant_f64  # noqa: F401

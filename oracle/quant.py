@@ -38,8 +38,11 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode_rne(v: np.ndarray) -> np.ndarray:
-    """float32 values with |v| <= 448 -> E4M3FN codes, round to nearest even."""
-    v = np.asarray(v, dtype=np.float32)
+    """float32 or float64 values with |v| <= 448 -> E4M3FN codes, round to
+    nearest even (other dtypes are taken as float32)."""
+    v = np.asarray(v)
+    if v.dtype != np.float64:
+        v = v.astype(np.float32)
     if np.any(~np.isfinite(v)) or np.any(np.abs(v) > E4M3_MAX):
         raise ValueError("E4M3 encoding needs finite values with |v| <= 448")
     a = np.abs(v.astype(np.float64))

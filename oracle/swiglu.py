@@ -9,74 +9,125 @@ performance"): the gate/up output C [R][2I] bf16 holds the gate in columns
 
     h[r, i] = silu(C[r, i]) * C[r, I + i],    silu(g) = g / (1 + exp(-g)),
 
-quantized per (row, 128) group exactly as oracle/quant.py does for tokens
-(s = amax/448 in fp32, codes by round to nearest even of clip(h/s, +-448)).
+quantized per (row, 128) group as oracle/quant.py does for tokens: the
+scale s = amax|h| / 448 (1 for an all-zero group), the code the E4M3FN
+round-to-nearest-even of clip(h / s, +-448).
 
-Since a float decides the integer codes, both sides compute h with one
-fixed fp32 sequence (IEEE single operations, no fused multiply-add):
-    x = -g; clamp to [-88, 89] (at the top the scaling below overflows to
-        inf, so silu is g / inf = -0; at the bottom e^x is far below 2^-24
-        and 1 + e^x rounds to 1, whatever happens to its denormals)
-    n = rint(x * log2(e)); r = (x - n * L_hi) - n * L_lo   (Cody and Waite's
-        two-constant reduction, L_hi + L_lo = ln 2, L_hi with 12 significant
-        bits so that n * L_hi is exact)
-    p = Horner's rule for the Taylor polynomial of e^r to degree 7
-    e = ldexp(p, n)          (exact scaling; inf above, 0 below the range)
-    silu = g / (1 + e);  h = silu * up
-The degree-7 Taylor remainder on |r| <= ln2/2 is below 2^-27 relative, so
-the fp32 exp is within a couple of units in the last place of e^x.
+The oracle is that definition in fp64 with the library exp (`swiglu_f64`,
+`swiglu_quant_f64`).  A GPU computes h in fp32, so near an E4M3 rounding
+midpoint, and in the last bits of the scale, more than one result is
+correct.  `check_swiglu_quant` therefore accepts a GPU result exactly when
+it is what the definition gives for values within a stated distance of the
+fp64 ones:
+
+  * h' is admissible for an element when |h' - h| <= H_REL * |h| +
+    H_ABS * |u|.  H_REL = 2^-20 (8 fp32 units in the last place) covers an
+    fp32 evaluation of silu(g) * u with an exp and a reciprocal accurate to
+    about an ulp each; H_ABS = 2^-118 covers the range where e^-g
+    overflows fp32 (g below about -88.7, where silu(g) rounds to -0 although
+    its magnitude is below 2^-120, or where the reciprocal of 1 + e^-g is
+    subnormal).
+  * the scale s' of a group is admissible when |s' - amax/448| <= S_REL *
+    amax/448 + H_ABS * max|u| / 448 (amax of admissible h' can differ from
+    the fp64 amax by no more than that), or when s' = 1 and every h of the
+    group is within H_ABS * |u| of zero.
+  * a code is admissible when its value is the E4M3 round-to-nearest-even of
+    clip(v, +-448) for some v with |v - h/s'| <= (H_REL * |h| + H_ABS * |u|)
+    / s' + Q_REL * |h/s'| (the quotient by s' itself rounded in fp32).
+    Rounding is monotone, so the admissible values form one interval,
+    [rne(lo), rne(hi)]; the code's value must lie in it (+0 and -0 are the
+    same value).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
+from .formats import e4m3_table
 from .quant import E4M3_MAX, bf16_bits_to_f32, e4m3_encode_rne
 
-F = np.float32
-LOG2E = F(1.4426950408889634)
-L_HI = F(0.693359375)               # 12 significant bits: n * L_HI is exact for |n| < 2^12
-L_LO = F(0.6931471805599453 - 0.693359375)
-TAYLOR = [F(1.0 / np.prod(np.arange(1, k + 1, dtype=np.float64))) for k in range(8)]  # 1/k!, k = 0..7
-X_MIN, X_MAX = F(-88.0), F(89.0)
+H_REL = 2.0 ** -20
+H_ABS = 2.0 ** -118
+S_REL = 2.0 ** -19
+Q_REL = 2.0 ** -21
 
 
-def exp_f32(x: np.ndarray) -> np.ndarray:
-    """e^x by the fixed fp32 sequence above (inputs float32)."""
-    x = np.clip(np.asarray(x, dtype=F), X_MIN, X_MAX).astype(F)
-    n = np.rint((x * LOG2E).astype(F)).astype(F)
-    r = ((x - (n * L_HI).astype(F)).astype(F) - (n * L_LO).astype(F)).astype(F)
-    p = np.full(x.shape, TAYLOR[7], dtype=F)
-    for k in range(6, -1, -1):
-        p = ((p * r).astype(F) + TAYLOR[k]).astype(F)
-    with np.errstate(over="ignore", under="ignore"):
-        return np.ldexp(p, n.astype(np.int32)).astype(F)
-
-
-def swiglu_f32(g: np.ndarray, u: np.ndarray) -> np.ndarray:
-    g = np.asarray(g, dtype=F)
-    u = np.asarray(u, dtype=F)
-    e = exp_f32(-g)
+def silu_f64(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + e^-g) in fp64 (for g below about -709 e^-g is inf
+    and the quotient -0, whose true magnitude is below 2^-1000)."""
+    g = np.asarray(g, dtype=np.float64)
     with np.errstate(over="ignore"):
-        d = (F(1.0) + e).astype(F)
-        silu = (g / d).astype(F)
-    return (silu * u).astype(F)
+        return g / (1.0 + np.exp(-g))
 
 
-def swiglu_quant(C_bits: np.ndarray, layout: int):
-    """C bf16 bits [R][2I] -> (codes uint8 [R][I], scales float32 flat in
-    `layout`: row-major [R][I/128] or M-major [I/128][R])."""
-    C = bf16_bits_to_f32(C_bits)
+def swiglu_f64(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u in fp64."""
+    return silu_f64(g) * np.asarray(u, dtype=np.float64)
+
+
+def _split(C_bits: np.ndarray):
+    C = bf16_bits_to_f32(C_bits).astype(np.float64)
     R, N2 = C.shape
     I = N2 // 2
     if N2 % 2 or I % 128:
         raise ValueError("C must be [R][2I] with I a multiple of 128")
-    h = swiglu_f32(C[:, :I], C[:, I:])
+    return C[:, :I], C[:, I:], R, I
+
+
+def swiglu_quant_f64(C_bits: np.ndarray, layout: int):
+    """C bf16 bits [R][2I] -> (codes uint8 [R][I], scales float64 flat in
+    `layout`: row-major [R][I/128] or M-major [I/128][R]), the definition
+    evaluated in fp64: s = amax/448 (1 if amax = 0), code = RNE(clip(h/s))."""
+    g, u, R, I = _split(C_bits)
+    h = swiglu_f64(g, u)
     G = I // 128
     hg = h.reshape(R, G, 128)
     amax = np.max(np.abs(hg), axis=2)
-    s = np.where(amax > 0, amax / F(E4M3_MAX), F(1.0)).astype(F)
-    v = np.clip((hg / s[:, :, None]).astype(F), F(-E4M3_MAX), F(E4M3_MAX))
+    s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    v = np.clip(hg / s[:, :, None], -E4M3_MAX, E4M3_MAX)
     codes = e4m3_encode_rne(v).reshape(R, I)
     SA = s.reshape(-1) if layout == 0 else s.T.copy().reshape(-1)
-    return codes, SA.astype(F)
+    return codes, SA
+
+
+def check_swiglu_quant(C_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, layout: int) -> dict:
+    """Admissibility of a result (codes uint8 [R][I], fp32 scales flat in
+    `layout`) against the fp64 definition, with the bounds of the module
+    docstring.  Returns counts: bad_scales, bad_codes, nan (codes or scales
+    that are NaN), ambiguous (elements for which more than one code value is
+    admissible), elements, and max_scale_rel (the largest relative distance
+    of an accepted scale from amax/448)."""
+    g, u, R, I = _split(C_bits)
+    G = I // 128
+    codes = np.asarray(codes, dtype=np.uint8).reshape(R, I)
+    s_in = np.asarray(scales, dtype=np.float32).reshape(-1).astype(np.float64)
+    if s_in.size != R * G:
+        raise ValueError("scales must hold R * I/128 values")
+    sg = s_in.reshape(R, G) if layout == 0 else s_in.reshape(G, R).T
+    h = swiglu_f64(g, u)
+    au = np.abs(u)
+    slack = H_REL * np.abs(h) + H_ABS * au                     # per element
+    hg = np.abs(h).reshape(R, G, 128)
+    amax = hg.max(axis=2)
+    umax = au.reshape(R, G, 128).max(axis=2)
+    ref = amax / E4M3_MAX
+    tiny = np.all(hg <= (H_ABS * au).reshape(R, G, 128), axis=2)  # the group may read as all zero
+    nan_s = ~np.isfinite(sg) | (sg <= 0)
+    ok_s = (np.abs(sg - ref) <= S_REL * ref + H_ABS * umax / E4M3_MAX) | (tiny & (sg == 1.0))
+    ok_s &= ~nan_s
+    sgf = np.where(nan_s, 1.0, sg)
+    s_el = np.repeat(sgf, 128, axis=1)
+    c = h / s_el
+    rad = slack / s_el + Q_REL * np.abs(c)
+    lo = np.clip(c - rad, -E4M3_MAX, E4M3_MAX)
+    hi = np.clip(c + rad, -E4M3_MAX, E4M3_MAX)
+    lut = e4m3_table()
+    vlo = lut[e4m3_encode_rne(lo)]
+    vhi = lut[e4m3_encode_rne(hi)]
+    nan_c = (codes & 0x7F) == 0x7F
+    val = lut[np.where(nan_c, 0, codes)]
+    ok_c = (val >= vlo) & (val <= vhi) & ~nan_c
+    rel = np.where(ok_s & (ref > 0), np.abs(sg - ref) / np.where(ref > 0, ref, 1.0), 0.0)
+    return {"bad_scales": int((~ok_s).sum()), "bad_codes": int((~ok_c).sum()),
+            "nan": int(nan_c.sum() + nan_s.sum()), "ambiguous": int((vlo != vhi).sum()),
+            "elements": int(R * I), "max_scale_rel": float(rel.max()) if rel.size else 0.0}
