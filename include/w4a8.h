@@ -200,12 +200,15 @@ int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of
  * A_fp8_dev     out uint8 [R][I] E4M3FN codes.  16-byte aligned.
  * a_scales_dev  out fp32 per (row, 128-column group) in a_scale_layout
  *               (row-major [R][I/128] or M-major [I/128][R]).  4-byte aligned.
- * h = silu(g) * u = (g / (1 + e^-g)) * u in fp32 by a fixed sequence of IEEE
- * single operations (e^x: Cody and Waite's two-constant reduction with
- * ln2 = 0.693359375 + (ln2 - 0.693359375), a degree-7 Taylor polynomial by
- * Horner's rule, exact scaling by 2^n; x clamped to [-88, 89]; no fused
- * multiply-add), then per group s = amax|h| / 448 (1 if all zero) and the
- * E4M3FN code of clip(h / s, +-448), round to nearest even, sign kept.
+ * h = silu(g) * u = (g / (1 + e^-g)) * u, evaluated in fp32 with the
+ * hardware exponential and reciprocal (within about five fp32 units in the
+ * last place of the exact value; where e^-g overflows fp32, g below about
+ * -88.7, silu is -0); then per group s = amax|h| / 448 (1 if all zero) and
+ * the E4M3FN code of clip(h * (1/s), +-448), round to nearest even.  Near an
+ * E4M3 rounding midpoint the fp32 evaluation may pick either neighbour: the
+ * result is the definition's for values within 2^-20 relative of the exact
+ * ones, not bit-reproducible by another evaluation order.  Deterministic:
+ * the same input gives the same bytes.
  * Limits: R >= 0, I % 128 == 0, 128 <= I <= W4A8_MAX_K.  R == 0 does nothing.
  */
 int w4a8_swiglu_quant(const uint16_t* C_bf16_dev, int R, int I, uint8_t* A_fp8_dev, float* a_scales_dev,

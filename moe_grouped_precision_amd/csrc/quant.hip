@@ -99,40 +99,35 @@ quant_gather_kernel(const uint16_t* __restrict__ x, int K, const int32_t* __rest
   }
 }
 
-// e^x by one fixed fp32 sequence, the same on both sides of the parity test:
-// Cody and Waite's two-constant reduction x = n ln2 + r (L_HI has 9
-// significant bits, so n * L_HI is exact for |n| <= 129), e^r by Horner's
-// rule on its Taylor polynomial to degree 7 (remainder below 2^-27 relative
-// for |r| <= ln2 / 2), exact scaling by 2^n.  x is clamped to [-88, 89]: at
-// the top the scaling overflows to inf, at the bottom e^x is far below 2^-24.
-// Separate rounded operations throughout (no fused multiply-add).
-constexpr float kLog2e = (float)1.4426950408889634;
-constexpr float kLnHi = 0.693359375f;
-constexpr float kLnLo = (float)(0.6931471805599453 - 0.693359375);
-__device__ __forceinline__ float exp_seq(float x) {
-#pragma clang fp contract(off)
-  x = fminf(fmaxf(x, -88.0f), 89.0f);
+// h = silu(g) * u = g / (1 + e^-g) * u in fp32 with the hardware exponential
+// and reciprocal: e^-g = 2^n * 2^(r log2 e) with n = rint(-g log2 e) and
+// r = -g - n ln2 by two fused multiply-adds (ln2 split into its fp32 value
+// and the fp32 value of the rest), so the argument of v_exp_f32 lies in
+// [-1/2, 1/2] and carries no error from the size of g; 2^n by an exact
+// ldexp.  -g is clamped to [-104, 104]: above about 88.7 e^-g overflows to
+// inf and silu to -0 (its magnitude is below 2^-120 there), below -104 it
+// underflows and silu is g.  The result is within about five fp32 units in
+// the last place of silu(g) * u (exp, reciprocal, three roundings).
+constexpr float kLog2e = 1.44269502162933349609375f;   // fp32(log2 e)
+constexpr float kLn2Hi = 0.693147182464599609375f;     // fp32(ln 2)
+constexpr float kLn2Lo = -1.9046542121259336e-09f;     // fp32(ln 2 - kLn2Hi)
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+  const float x = fminf(fmaxf(-g, -104.0f), 104.0f);
   const float n = rintf(x * kLog2e);
-  const float r = (x - n * kLnHi) - n * kLnLo;
-  float p = (float)(1.0 / 5040.0);
-  p = p * r + (float)(1.0 / 720.0);
-  p = p * r + (float)(1.0 / 120.0);
-  p = p * r + (float)(1.0 / 24.0);
-  p = p * r + (float)(1.0 / 6.0);
-  p = p * r + (float)(1.0 / 2.0);
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  return ldexpf(p, (int)n);
+  const float r = fmaf(-n, kLn2Lo, fmaf(-n, kLn2Hi, x));
+  const float e = ldexpf(__builtin_amdgcn_exp2f(r * kLog2e), (int)n);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // SwiGLU of the gate/up output and its E4M3 requantization: one workgroup
 // per row; 8 lanes per 128-column group, 16 columns of gate (columns 0 ..
-// I-1) and the same 16 of up (columns I .. 2I-1) per lane; h = silu(g) * u =
-// (g / (1 + e^-g)) * u in fp32, then the quantization above.
+// I-1) and the same 16 of up (columns I .. 2I-1) per lane; h as above, then
+// per group s = amax / 448 (IEEE division; 1 for an all-zero group), v =
+// clip(h * (1/s), +-448) and the E4M3FN code of v by the hardware conversion
+// (v_cvt_pk_fp8_f32: round to nearest even, OCP E4M3 on gfx950).
 __global__ void __launch_bounds__(512)
 swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __restrict__ A, float* __restrict__ SA,
                     int layout) {
-#pragma clang fp contract(off)
   // M-major scales: consecutive rows on one XCD (see quant_gather_kernel)
   const int r = (layout == 0 || (R & 7)) ? (int)blockIdx.x
                                          : (int)((blockIdx.x & 7) * (R >> 3) + (blockIdx.x >> 3));
@@ -153,9 +148,7 @@ swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __res
     for (int i = 0; i < 16; ++i) {
       const uint32_t gb = (i & 1) ? (gw[i >> 1] & 0xffff0000u) : (gw[i >> 1] << 16);
       const uint32_t ub = (i & 1) ? (uw[i >> 1] & 0xffff0000u) : (uw[i >> 1] << 16);
-      const float gv = __uint_as_float(gb), uv = __uint_as_float(ub);
-      const float d = 1.0f + exp_seq(-gv);
-      h[i] = __fdiv_rn(gv, d) * uv;
+      h[i] = swiglu_f32(__uint_as_float(gb), __uint_as_float(ub));
     }
     float m = 0.f;
 #pragma unroll
@@ -164,13 +157,17 @@ swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __res
     m = fmaxf(m, __shfl_xor(m, 2, 8));
     m = fmaxf(m, __shfl_xor(m, 4, 8));
     const float s = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
+    const float inv = __fdiv_rn(1.0f, s);
+    int c[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float y = fminf(fmaxf(__fdiv_rn(h[i], s), -448.0f), 448.0f);
-      c[i >> 2] |= e4m3_rne(y) << (8 * (i & 3));
+    for (int i = 0; i < 4; ++i) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(h[4 * i + j] * inv, -448.0f), 448.0f);
+      c[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      c[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c[i], true);
     }
-    const v4u out = {c[0], c[1], c[2], c[3]};
+    const v4u out = {(uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]};
     __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(A + (size_t)r * I + g * 128 + lane8 * 16));
     if (lane8 == 0) SA[layout ? (size_t)g * R + r : (size_t)r * G + g] = s;
   }

@@ -17,18 +17,55 @@ def bits_of(c: torch.Tensor) -> np.ndarray:
 
 def parity_error(gpu_bits: np.ndarray, ref_bits: np.ndarray, rms_ref: float | None = None) -> float:
     """Largest elementwise |g - r| / max(rms(ref), |r|); inf if any NaN/inf disagrees."""
+    return parity_report(gpu_bits, ref_bits, rms_ref)["err"]
+
+
+MAX_MISMATCH_FRAC = 2e-2   # elements whose bf16 bits differ from the oracle's
+MAX_ULP_LARGE = 1          # bf16 ulps, on elements with |ref| >= rms(ref)
+
+
+def parity_report(gpu_bits: np.ndarray, ref_bits: np.ndarray, rms_ref: float | None = None) -> dict:
+    """err: the normalised maximum above; mismatches: elements whose bits
+    differ; max_ulp: largest |g - r| in bf16 ulps of r (over all elements, and
+    over those with |r| >= rms as max_ulp_large)."""
     g = bf16_bits_to_f64(gpu_bits)
     r = bf16_bits_to_f64(ref_bits)
     if g.shape != r.shape:
         raise AssertionError(f"shape {g.shape} vs {r.shape}")
-    if g.size == 0:
-        return 0.0
+    n = int(g.size)
+    if n == 0:
+        return {"err": 0.0, "mismatches": 0, "n": 0, "max_ulp": 0.0, "max_ulp_large": 0.0}
     if not np.all(np.isfinite(g)) or not np.all(np.isfinite(r)):
-        return float("inf")
+        return {"err": float("inf"), "mismatches": n, "n": n, "max_ulp": float("inf"),
+                "max_ulp_large": float("inf")}
     rms = float(np.sqrt(np.mean(r * r))) if rms_ref is None else rms_ref
     den = np.maximum(rms, np.abs(r))
     den = np.where(den == 0, 1.0, den)
-    return float(np.max(np.abs(g - r) / den))
+    diff = np.abs(g - r)
+    # one bf16 ulp of r: 2^(exponent - 7), at least the subnormal quantum 2^-133
+    _, p = np.frexp(np.abs(r))
+    ulp = np.ldexp(1.0, np.maximum(p - 8, -133))
+    ulps = diff / ulp
+    large = np.abs(r) >= rms
+    return {"err": float(np.max(diff / den)),
+            "mismatches": int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits))),
+            "n": n, "max_ulp": float(ulps.max()),
+            "max_ulp_large": float(ulps[large].max()) if large.any() else 0.0}
+
+
+def assert_parity(gpu_bits: np.ndarray, ref_bits: np.ndarray, label: str, rms_ref: float | None = None) -> dict:
+    """Print the parity report and assert the bar: normalised error <= TOL,
+    at most MAX_ULP_LARGE bf16 ulps on elements at least rms in size, and at
+    most MAX_MISMATCH_FRAC of the elements differing in their bits (so that a
+    drift from rare one-ulp flips to widespread ones shows)."""
+    rep = parity_report(gpu_bits, ref_bits, rms_ref)
+    frac = rep["mismatches"] / max(rep["n"], 1)
+    print(f"{label}: parity_error={rep['err']:.3e} mismatches={rep['mismatches']}/{rep['n']} "
+          f"({frac:.2e}) max_ulp={rep['max_ulp']:.3g} max_ulp_large={rep['max_ulp_large']:.3g}", flush=True)
+    assert rep["err"] <= TOL, rep
+    assert rep["max_ulp_large"] <= MAX_ULP_LARGE, rep
+    assert frac <= MAX_MISMATCH_FRAC, rep
+    return rep
 
 
 def to_device(p, device="cuda"):

@@ -4,10 +4,10 @@ against the oracles chained the same way (an integration check):
     tokens --quantize_gather--> A1, SA1 --grouped_gemm (gate/up)--> C1
       --swiglu_quant--> A2, SA2 --grouped_gemm (down)--> C2 --combine--> out
 
-Each GPU stage is bit-exact or within the GEMM tolerance of its oracle on the
-same inputs (the stage tests); here every GPU stage consumes the GPU's own
-previous output and the oracle chain its own, so the GEMMs' fp32 rounding
-can move an E4M3 code of the SwiGLU requantization by one step.  The check
+Each GPU stage matches its oracle on the same inputs (the stage tests);
+here every GPU stage consumes the GPU's own previous output and the oracle
+chain its own (the SwiGLU step in fp64), so the GEMMs' fp32 rounding and the
+fp32 SwiGLU can move an E4M3 code of the requantization by one step.  The check
 is the chained error: per element within 3e-2 of max(rms, |ref|), and 5e-3
 in the mean."""
 
@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from oracle import combine_ref, grouped_gemm_bf16, quantize_gather, route_ref, swiglu_quant
+from oracle import combine_ref, grouped_gemm_bf16, quantize_gather, route_ref, swiglu_quant_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,8 @@ def test_moe_layer_chain(gpu_lib, layout):
     assert np.array_equal(off.cpu().numpy(), off_r) and np.array_equal(ros.cpu().numpy(), ros_r)
     a1, sa1 = quantize_gather(_bits(x), ros_r, k, R, layout)
     c1 = grouped_gemm_bf16(a1, sa1, layout, B1.numpy(), SB1.numpy(), off_r)
-    a2, sa2 = swiglu_quant(c1, layout)
+    a2, sa2 = swiglu_quant_f64(c1, layout)
+    sa2 = sa2.astype(np.float32)            # the boundary's scale format
     c2 = grouped_gemm_bf16(a2, sa2, layout, B2.numpy(), SB2.numpy(), off_r)
     ref = combine_ref(c2, ros_r, wts.numpy(), T, k)
 
