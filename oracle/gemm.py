@@ -39,22 +39,25 @@ def _np(x):
     return np.asarray(x)
 
 
-def decode_activations(a_codes, sa_rows) -> np.ndarray:
-    """E4M3 codes [r, K] and fp32 scales [r, K/128] -> fp64 [r, K]."""
+def decode_activations(a_codes, sa_rows, absolute: bool = False) -> np.ndarray:
+    """E4M3 codes [r, K] and fp32 scales [r, K/128] -> fp64 [r, K] (their
+    magnitudes with absolute=True)."""
     a = _LUT8[_np(a_codes).astype(np.intp)]
     s = _np(sa_rows).astype(np.float64)
-    return a * np.repeat(s, 128, axis=1)
+    out = a * np.repeat(s, 128, axis=1)
+    return np.abs(out) if absolute else out
 
 
-def decode_weights(b_packed, sb) -> np.ndarray:
-    """Packed E2M1 [N, K/2] and E8M0 [N, K/32] -> fp64 [N, K]."""
+def decode_weights(b_packed, sb, absolute: bool = False) -> np.ndarray:
+    """Packed E2M1 [N, K/2] and E8M0 [N, K/32] -> fp64 [N, K] (their
+    magnitudes with absolute=True)."""
     b = _np(b_packed).astype(np.uint8)
     n, kh = b.shape
     codes = np.empty((n, 2 * kh), dtype=np.intp)
     codes[:, 0::2] = b & 0x0F          # even k: low nibble
     codes[:, 1::2] = b >> 4            # odd k: high nibble
-    w = _LUT4[codes]
-    return w * np.repeat(e8m0_value(_np(sb)), 32, axis=1)
+    w = _LUT4[codes] * np.repeat(e8m0_value(_np(sb)), 32, axis=1)
+    return np.abs(w) if absolute else w
 
 
 def sa_rows(sa, layout: int, rows: np.ndarray, R: int, K: int) -> np.ndarray:
@@ -74,8 +77,10 @@ def expert_gemm_f64(a_codes, sa_r, b_packed, sb) -> np.ndarray:
     return decode_activations(a_codes, sa_r) @ decode_weights(b_packed, sb).T
 
 
-def grouped_gemm_f64(A, SA, layout, B, SB, offsets, chunk_rows: int = 8192) -> np.ndarray:
-    """Exact-product fp64 grouped GEMM, [R, N]."""
+def grouped_gemm_f64(A, SA, layout, B, SB, offsets, chunk_rows: int = 8192, absolute: bool = False) -> np.ndarray:
+    """Exact-product fp64 grouped GEMM, [R, N].  With absolute=True, the sum
+    of the magnitudes of the same products, sum_k |a_k w_k| per output: the
+    scale of the rounding error of any evaluation of the sum."""
     A = _np(A)
     B = _np(B)
     SB = _np(SB)
@@ -93,11 +98,11 @@ def grouped_gemm_f64(A, SA, layout, B, SB, offsets, chunk_rows: int = 8192) -> n
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
-        wd = decode_weights(B[e], SB[e])
+        wd = decode_weights(B[e], SB[e], absolute)
         for c0 in range(lo, hi, chunk_rows):
             c1 = min(hi, c0 + chunk_rows)
             rows = np.arange(c0, c1)
-            ad = decode_activations(A[c0:c1], sa_rows(SA, layout, rows, R, K))
+            ad = decode_activations(A[c0:c1], sa_rows(SA, layout, rows, R, K), absolute)
             out[c0:c1] = ad @ wd.T
     return out
 
@@ -107,13 +112,14 @@ def grouped_gemm_bf16(A, SA, layout, B, SB, offsets) -> np.ndarray:
     return bf16_rne_bits(grouped_gemm_f64(A, SA, layout, B, SB, offsets))
 
 
-def rows_gemm_f64(a_rows, sa_r, expert_of_row, B, SB, cols=None) -> np.ndarray:
+def rows_gemm_f64(a_rows, sa_r, expert_of_row, B, SB, cols=None, absolute: bool = False) -> np.ndarray:
     """fp64 outputs for a sample of rows (each with its own expert), [r, len(cols)].
 
     ``a_rows``  E4M3 codes of the sampled rows [r, K]
     ``sa_r``    their scales [r, K/128]
     ``expert_of_row`` the expert each sampled row belongs to
     ``cols``    optional subset of output columns (default: all N)
+    ``absolute`` sum the magnitudes of the products instead
     """
     a_rows = _np(a_rows)
     sa_r = _np(sa_r)
@@ -123,6 +129,6 @@ def rows_gemm_f64(a_rows, sa_r, expert_of_row, B, SB, cols=None) -> np.ndarray:
     out = np.empty((len(ex), len(cols)), dtype=np.float64)
     for e in np.unique(ex):
         sel = np.nonzero(ex == e)[0]
-        wd = decode_weights(_np(B[int(e)])[cols], _np(SB[int(e)])[cols])
-        out[sel] = decode_activations(a_rows[sel], sa_r[sel]) @ wd.T
+        wd = decode_weights(_np(B[int(e)])[cols], _np(SB[int(e)])[cols], absolute)
+        out[sel] = decode_activations(a_rows[sel], sa_r[sel], absolute) @ wd.T
     return out

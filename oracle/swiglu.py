@@ -96,7 +96,8 @@ def check_swiglu_quant(C_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray
     docstring.  Returns counts: bad_scales, bad_codes, nan (codes or scales
     that are NaN), ambiguous (elements for which more than one code value is
     admissible), elements, and max_scale_rel (the largest relative distance
-    of an accepted scale from amax/448)."""
+    of an accepted scale from amax/448, over groups not within the floor of
+    zero)."""
     g, u, R, I = _split(C_bits)
     G = I // 128
     codes = np.asarray(codes, dtype=np.uint8).reshape(R, I)
@@ -127,7 +128,7 @@ def check_swiglu_quant(C_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray
     nan_c = (codes & 0x7F) == 0x7F
     val = lut[np.where(nan_c, 0, codes)]
     ok_c = (val >= vlo) & (val <= vhi) & ~nan_c
-    rel = np.where(ok_s & (ref > 0), np.abs(sg - ref) / np.where(ref > 0, ref, 1.0), 0.0)
+    rel = np.where(ok_s & ~tiny, np.abs(sg - ref) / np.where(ref > 0, ref, 1.0), 0.0)
     return {"bad_scales": int((~ok_s).sum()), "bad_codes": int((~ok_c).sum()),
             "nan": int(nan_c.sum() + nan_s.sum()), "ambiguous": int((vlo != vhi).sum()),
             "elements": int(R * I), "max_scale_rel": float(rel.max()) if rel.size else 0.0}

@@ -20,51 +20,74 @@ def parity_error(gpu_bits: np.ndarray, ref_bits: np.ndarray, rms_ref: float | No
     return parity_report(gpu_bits, ref_bits, rms_ref)["err"]
 
 
-MAX_MISMATCH_FRAC = 2e-2   # elements whose bf16 bits differ from the oracle's
 MAX_ULP_LARGE = 1          # bf16 ulps, on elements with |ref| >= rms(ref)
 
 
-def parity_report(gpu_bits: np.ndarray, ref_bits: np.ndarray, rms_ref: float | None = None) -> dict:
+def fp32_sum_eps(K: int) -> float:
+    """Relative bound on the fp32 accumulation error of one output, as a
+    fraction of sum_k |a_k w_k|: the matrix core's sum of a 128-K group
+    (exact products; allow 16 roundings), one rounding of the group partial,
+    one rounding per promotion into the accumulator and one for the addition
+    of the K halves: (2 G + 16) units of 2^-24 with G = K / 128 groups."""
+    return (2 * (K // 128) + 16) * 2.0 ** -24
+
+
+def _bf16_ulp(x: np.ndarray) -> np.ndarray:
+    _, p = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(p - 8, -133))
+
+
+def parity_report(gpu_bits: np.ndarray, ref_bits: np.ndarray, rms_ref: float | None = None,
+                  exact: np.ndarray | None = None, abs_sum: np.ndarray | None = None, K: int | None = None) -> dict:
     """err: the normalised maximum above; mismatches: elements whose bits
     differ; max_ulp: largest |g - r| in bf16 ulps of r (over all elements, and
-    over those with |r| >= rms as max_ulp_large)."""
+    over those with |r| >= rms as max_ulp_large).  With the fp64 exact values
+    and the magnitude sums of their products (oracle grouped_gemm_f64 with
+    absolute=False / True) and K: beyond_fp32 = elements farther from the
+    exact value than an fp32 accumulation (fp32_sum_eps(K) * abs_sum) followed
+    by one bf16 rounding can be."""
     g = bf16_bits_to_f64(gpu_bits)
     r = bf16_bits_to_f64(ref_bits)
     if g.shape != r.shape:
         raise AssertionError(f"shape {g.shape} vs {r.shape}")
     n = int(g.size)
+    rep = {"err": 0.0, "mismatches": 0, "n": n, "max_ulp": 0.0, "max_ulp_large": 0.0, "beyond_fp32": 0}
     if n == 0:
-        return {"err": 0.0, "mismatches": 0, "n": 0, "max_ulp": 0.0, "max_ulp_large": 0.0}
+        return rep
     if not np.all(np.isfinite(g)) or not np.all(np.isfinite(r)):
-        return {"err": float("inf"), "mismatches": n, "n": n, "max_ulp": float("inf"),
-                "max_ulp_large": float("inf")}
+        rep.update(err=float("inf"), mismatches=n, max_ulp=float("inf"), max_ulp_large=float("inf"), beyond_fp32=n)
+        return rep
     rms = float(np.sqrt(np.mean(r * r))) if rms_ref is None else rms_ref
     den = np.maximum(rms, np.abs(r))
     den = np.where(den == 0, 1.0, den)
     diff = np.abs(g - r)
-    # one bf16 ulp of r: 2^(exponent - 7), at least the subnormal quantum 2^-133
-    _, p = np.frexp(np.abs(r))
-    ulp = np.ldexp(1.0, np.maximum(p - 8, -133))
-    ulps = diff / ulp
+    ulps = diff / _bf16_ulp(r)
     large = np.abs(r) >= rms
-    return {"err": float(np.max(diff / den)),
-            "mismatches": int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits))),
-            "n": n, "max_ulp": float(ulps.max()),
-            "max_ulp_large": float(ulps[large].max()) if large.any() else 0.0}
+    rep.update(err=float(np.max(diff / den)),
+               mismatches=int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits))),
+               max_ulp=float(ulps.max()), max_ulp_large=float(ulps[large].max()) if large.any() else 0.0)
+    if exact is not None:
+        acc_err = fp32_sum_eps(K) * np.asarray(abs_sum, dtype=np.float64)
+        bound = acc_err + 0.5 * _bf16_ulp(np.abs(exact) + acc_err)
+        rep["beyond_fp32"] = int(np.count_nonzero(np.abs(g - exact) > bound))
+    return rep
 
 
-def assert_parity(gpu_bits: np.ndarray, ref_bits: np.ndarray, label: str, rms_ref: float | None = None) -> dict:
+def assert_parity(gpu_bits: np.ndarray, ref_bits: np.ndarray, label: str, rms_ref: float | None = None,
+                  exact: np.ndarray | None = None, abs_sum: np.ndarray | None = None, K: int | None = None) -> dict:
     """Print the parity report and assert the bar: normalised error <= TOL,
-    at most MAX_ULP_LARGE bf16 ulps on elements at least rms in size, and at
-    most MAX_MISMATCH_FRAC of the elements differing in their bits (so that a
-    drift from rare one-ulp flips to widespread ones shows)."""
-    rep = parity_report(gpu_bits, ref_bits, rms_ref)
+    at most MAX_ULP_LARGE bf16 ulps on elements at least rms in size, and --
+    given the exact values -- no element beyond what fp32 accumulation and
+    one bf16 rounding allow (so a drift from rare one-ulp flips to
+    widespread ones shows)."""
+    rep = parity_report(gpu_bits, ref_bits, rms_ref, exact, abs_sum, K)
     frac = rep["mismatches"] / max(rep["n"], 1)
     print(f"{label}: parity_error={rep['err']:.3e} mismatches={rep['mismatches']}/{rep['n']} "
-          f"({frac:.2e}) max_ulp={rep['max_ulp']:.3g} max_ulp_large={rep['max_ulp_large']:.3g}", flush=True)
+          f"({frac:.2e}) max_ulp={rep['max_ulp']:.3g} max_ulp_large={rep['max_ulp_large']:.3g} "
+          f"beyond_fp32={rep['beyond_fp32'] if exact is not None else '-'}", flush=True)
     assert rep["err"] <= TOL, rep
     assert rep["max_ulp_large"] <= MAX_ULP_LARGE, rep
-    assert frac <= MAX_MISMATCH_FRAC, rep
+    assert rep["beyond_fp32"] == 0, rep
     return rep
 
 

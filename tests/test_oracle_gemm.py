@@ -206,7 +206,7 @@ def test_bad_offsets_rejected():
 # planted mistakes: each mutation of the oracle must break the brute-force pin
 # --------------------------------------------------------------------------
 
-def _swap_nibbles(b, sb):
+def _swap_nibbles(b, sb, absolute=False):
     b = og._np(b).astype(np.uint8)
     n, kh = b.shape
     codes = np.empty((n, 2 * kh), dtype=np.intp)
@@ -218,23 +218,23 @@ def _swap_nibbles(b, sb):
 _ORIG_DECODE_WEIGHTS = og.decode_weights
 
 
-def _sb_off_by_block(b, sb):
+def _sb_off_by_block(b, sb, absolute=False):
     w = _ORIG_DECODE_WEIGHTS(b, sb)
     sbv = np.roll(oracle.e8m0_value(og._np(sb)), 1, axis=1)
     return w / np.repeat(oracle.e8m0_value(og._np(sb)), 32, axis=1) * np.repeat(sbv, 32, axis=1)
 
 
-def _drop_sa(a, s):
+def _drop_sa(a, s, absolute=False):
     return og._LUT8[og._np(a).astype(np.intp)]
 
 
-def _sa_wrong_row(a, s):
+def _sa_wrong_row(a, s, absolute=False):
     a8 = og._LUT8[og._np(a).astype(np.intp)]
     s = np.roll(og._np(s).astype(np.float64), 1, axis=0)
     return a8 * np.repeat(s, 128, axis=1)
 
 
-def _sign_loss(b, sb):
+def _sign_loss(b, sb, absolute=False):
     return np.abs(_ORIG_DECODE_WEIGHTS(b, sb))
 
 
@@ -263,3 +263,35 @@ def test_planted_transpose_is_caught():
     ad = og.decode_activations(A, SA.reshape(3, 1))
     wrong = bf16_rne_bits((ad @ wd.T).T)    # transposed result, same shape here
     assert not np.array_equal(wrong, want)
+
+
+def test_absolute_sum_bruteforce_and_invariants():
+    """absolute=True gives sum_k |a_k w_k| (the scale of any evaluation's
+    rounding error): equal to an exact rational sum of magnitudes on a tiny
+    case, >= |C| everywhere, equal to C when every product is nonnegative,
+    unchanged by flipping the sign of the weights."""
+    rng = np.random.default_rng(43)
+    A, SA, B, SB, off = random_case(rng, E=2, N=5, K=256, rows_per_expert=[2, 3])
+    got = grouped_gemm_f64(A, SA, 0, B, SB, off, absolute=True)
+    G = 2
+    for e in range(2):
+        for r in range(int(off[e]), int(off[e + 1])):
+            for n in range(5):
+                acc = Fraction(0)
+                for k in range(256):
+                    byte = int(B[e, n, k // 2])
+                    w = _dec4((byte >> (4 * (k % 2))) & 0xF)
+                    acc += abs(Fraction(_DEC8[A[r, k]]) * Fraction(float(SA[r * G + k // 128])) * Fraction(w)
+                               * Fraction(2) ** (int(SB[e, n, k // 32]) - 127))
+                assert abs(Fraction(got[r, n]) - acc) <= acc * Fraction(1, 2 ** 50)
+    C = grouped_gemm_f64(A, SA, 0, B, SB, off)
+    assert np.all(got >= np.abs(C) * (1 - 1e-15))
+    assert np.array_equal(grouped_gemm_f64(A, SA, 0, B ^ 0x88, SB, off, absolute=True), got)
+    Apos = A & 0x7F                                   # nonnegative activations
+    Bpos = B & 0x77                                   # nonnegative weights
+    Cp = grouped_gemm_f64(Apos, SA, 0, Bpos, SB, off)
+    np.testing.assert_allclose(grouped_gemm_f64(Apos, SA, 0, Bpos, SB, off, absolute=True), Cp, rtol=1e-14)
+    rows = np.array([0, 4])
+    ex = np.array([0, 1])
+    np.testing.assert_allclose(og.rows_gemm_f64(A[rows], SA.reshape(-1, 2)[rows], ex, B, SB, absolute=True),
+                               got[rows], rtol=1e-12)
