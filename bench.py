@@ -435,6 +435,48 @@ def measure_gemm_wide_pool(reps=5):
     return out
 
 
+def measure_gemm_swiglu(reps=10):
+    """The gate/up GEMM with the SwiGLU + E4M3 requantization epilogue
+    (w4a8_grouped_gemm_swiglu) on the large prefill gate/up workload (16384
+    tokens, top-8 biased routing over 32 experts, N = 2I = 4096, K = 6144,
+    M-major scales in and out), beside the same inputs through the plain
+    GEMM followed by w4a8_swiglu_quant.  MFMA roofline on 2 R N K."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+
+    w = Workload("prefill_gateup", 1, torch.device("cuda:0"))
+    w.route()
+    p = w.p
+    I = p.N // 2
+    A2 = torch.empty((p.R, I), dtype=torch.uint8, device="cuda")
+    SA2 = torch.empty((I // 128, p.R), dtype=torch.float32, device="cuda")
+
+    def fused(i):
+        w4a8.grouped_gemm_swiglu(w.A, w.SA, 1, w.Bs[i % w.nrot], w.SBs[i % w.nrot], w.off_d, 1, A2=A2, SA2=SA2)
+
+    def unfused(i):
+        w.gemm(i)
+        w4a8.swiglu_quant(w.C, 1, A=A2, SA=SA2)
+
+    ms = time_launches(fused, reps, warmup=3)
+    ms_u = time_launches(unfused, reps, warmup=3)
+    counts = w.counts_d.cpu().numpy()
+    flops = 2.0 * p.R * p.N * p.K
+    med = statistics.median(ms)
+    tfs = flops / (med * 1e-3) / 1e12
+    hit = int((counts > 0).sum())
+    nbytes = hit * p.N * p.K * (0.5 + 1 / 32) + p.R * p.K * (1 + 4 / 128) + p.R * I * (1 + 4 / 128) + 4 * (p.E + 1)
+    out = {"workload": w.describe() + ", SwiGLU + E4M3 requantization (M-major scales) in the epilogue",
+           "us_median": round(med * 1e3, 2), "us_p10_p90": [pct(ms, 10), pct(ms, 90)],
+           "unfused_gemm_plus_swiglu_quant_us_median": round(statistics.median(ms_u) * 1e3, 2),
+           "algorithmic_bytes": int(nbytes), "flop": flops, "tflops": round(tfs, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_FP8_PEAK_TFS, "unit": "TFLOP/s",
+                        "frac": round(tfs / MFMA_FP8_PEAK_TFS, 4)}}
+    w.free()
+    return out
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
@@ -495,9 +537,10 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        log("timing the activation quantizer, SwiGLU requantization, the top-k combine, "
-            "the routing prep over 6144 experts and the GEMM over 2048 experts")
-        extras = {"quantize_gather": measure_quantize_gather(), "swiglu_quant": measure_swiglu_quant(),
+        log("timing the fused gate/up + SwiGLU GEMM, the activation quantizer, SwiGLU requantization, "
+            "the top-k combine, the routing prep over 6144 experts and the GEMM over 2048 experts")
+        extras = {"grouped_gemm_swiglu": measure_gemm_swiglu(),
+                  "quantize_gather": measure_quantize_gather(), "swiglu_quant": measure_swiglu_quant(),
                   "combine": measure_combine(), "route_prep_wide_pool": measure_route_prep_wide(),
                   "grouped_gemm_wide_pool": measure_gemm_wide_pool()}
 

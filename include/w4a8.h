@@ -243,6 +243,38 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
                       uint16_t* C_bf16_dev, void* stream);
 
 /*
+ * w4a8_grouped_gemm_swiglu -- the gate/up projection with the step between
+ * the two projections fused into its epilogue (humming PR #129 "Results"
+ * and PR #58 "H200 performance" time gate/up and down as a pair): the
+ * grouped W4A8 GEMM of w4a8_grouped_gemm with N = 2I weight columns, then
+ * h = silu(gate) * up and its E4M3 requantization exactly as
+ * w4a8_swiglu_quant, but from the fp32 accumulators (no bf16 rounding of the
+ * gate/up output, which is never written).
+ *
+ * A_fp8_dev, a_scales_dev, a_scale_layout, expert_offsets_dev, E, K: as
+ *                    w4a8_grouped_gemm.
+ * B13_fp4_dev        uint8 [E][2I][K/2] packed E2M1: columns 0 .. I-1 the
+ *                    gate projection (w1), I .. 2I-1 the up projection (w3),
+ *                    the concatenated [w1; w3] layout.  16-byte aligned.
+ * b13_scales_e8m0_dev uint8 [E][2I][K/32] E8M0.  4-byte aligned.
+ * A2_fp8_dev         out uint8 [R][I] E4M3FN codes of h.  16-byte aligned.
+ * a2_scales_dev      out fp32 per (row, 128 columns of A2) in a2_scale_layout
+ *                    (row-major [R][I/128] or M-major [I/128][R], R =
+ *                    offsets[E]).  4-byte aligned.
+ * Per row and 128-column group: s = amax|h| / 448 (1 if all zero), codes =
+ * E4M3 round-to-nearest-even of clip(h * (1/s), +-448).  gate and up carry
+ * the GEMM's fp32 accumulation error; h is evaluated as in
+ * w4a8_swiglu_quant.  Only rows < R are written.  Every expert with rows
+ * runs as MFMA tiles of 256 output columns (the small-M streaming schedule
+ * is not used by this entry point).
+ * Limits: as w4a8_grouped_gemm with N = 2I; I % 128 == 0; 2I * K/2 < 2^31.
+ */
+int w4a8_grouped_gemm_swiglu(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                             const uint8_t* B13_fp4_dev, const uint8_t* b13_scales_e8m0_dev,
+                             const int32_t* expert_offsets_dev, int E, int I, int K, uint8_t* A2_fp8_dev,
+                             float* a2_scales_dev, int a2_scale_layout, void* stream);
+
+/*
  * w4a8_plan_params -- the plan rule's constants, written to out_host[0..n-1]
  * in this order: GRAN (m granularity), S_MAX, T_MAX, TN_STREAM (n granularity
  * of streaming work), TN_MFMA (n width of an MFMA work item), plan header

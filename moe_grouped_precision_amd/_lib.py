@@ -42,6 +42,8 @@ def _declare(lib):
     lib.w4a8_plan.restype = i32
     lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_grouped_gemm_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
+    lib.w4a8_grouped_gemm_swiglu.restype = i32
     lib.w4a8_swiglu_quant.argtypes = [vp, i32, i32, vp, vp, i32, vp]
     lib.w4a8_swiglu_quant.restype = i32
     lib.w4a8_combine.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp]
@@ -190,6 +192,40 @@ def grouped_gemm(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor
         _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
         _ptr(out), _stream()))
     return out
+
+
+def grouped_gemm_swiglu(A: torch.Tensor, SA: torch.Tensor, layout: int, B13: torch.Tensor, SB13: torch.Tensor,
+                        expert_offsets: torch.Tensor, layout2: int, A2: Optional[torch.Tensor] = None,
+                        SA2: Optional[torch.Tensor] = None):
+    """The gate/up GEMM with SwiGLU and E4M3 requantization in its epilogue:
+    (A2 uint8 [R, I] codes of silu(gate) * up, SA2 fp32 [R, I/128] for layout2
+    0 or [I/128, R] for layout2 1).  B13 uint8 [E, 2I, K/2] (gate columns
+    first), SB13 uint8 [E, 2I, K/32]; the rest as grouped_gemm."""
+    lib = load()
+    if A.dim() != 2 or B13.dim() != 3 or SB13.dim() != 3:
+        raise ValueError("A must be [R, K], B13 [E, 2I, K/2], SB13 [E, 2I, K/32]")
+    R, K = A.shape
+    E, N2, Kh = B13.shape
+    if Kh * 2 != K or N2 % 2 or SB13.shape != (E, N2, K // 32):
+        raise ValueError("inconsistent shapes between A, B13 and SB13")
+    I = N2 // 2
+    _need(A, "A", torch.uint8)
+    _need(SA, "a_scales", torch.float32, R * (K // 128))
+    _need(B13, "B13", torch.uint8)
+    _need(SB13, "b13_scales", torch.uint8)
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    if A2 is None:
+        A2 = torch.empty((R, I), dtype=torch.uint8, device=A.device)
+    if SA2 is None:
+        SA2 = torch.empty((R, I // 128) if layout2 == 0 else (I // 128, R), dtype=torch.float32, device=A.device)
+    _need(A2, "A2", torch.uint8, R * I)
+    _need(SA2, "a2_scales", torch.float32, R * (I // 128))
+    if R == 0:
+        return A2, SA2
+    _check("w4a8_grouped_gemm_swiglu", lib.w4a8_grouped_gemm_swiglu(
+        _ptr(A), _ptr(SA), int(layout), _ptr(B13), _ptr(SB13), _ptr(expert_offsets), E, I, K, _ptr(A2),
+        _ptr(SA2), int(layout2), _stream()))
+    return A2, SA2
 
 
 def quantize_gather(x: torch.Tensor, row_of_slot: torch.Tensor, top_k: int, R: int, layout: int,

@@ -185,9 +185,41 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
   st = device_info(&d);
   if (st != W4A8_OK) return st;
   w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev,
-                      C_bf16_dev, E, N, K, a_scale_layout};
+                      C_bf16_dev, E, N, K, a_scale_layout, nullptr, nullptr, 0, 0};
   hipError_t e = w4a8::launch_grouped_gemm(args, d->grid, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_grouped_gemm_swiglu(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                             const uint8_t* B13_fp4_dev, const uint8_t* b13_scales_e8m0_dev,
+                             const int32_t* expert_offsets_dev, int E, int I, int K, uint8_t* A2_fp8_dev,
+                             float* a2_scales_dev, int a2_scale_layout, void* stream) {
+  if (I < 128 || I % 128 || (int64_t)I > W4A8_MAX_N / 2)
+    return fail(W4A8_ERR_SHAPE, "I=%d must be a multiple of 128 in [128, %d]", I, W4A8_MAX_N / 2);
+  int st = check_gemm_shape(E, 2 * I, K);
+  if (st != W4A8_OK) return st;
+  if ((int64_t)2 * I * (K / 2) >= ((int64_t)1 << 31))
+    return fail(W4A8_ERR_SHAPE, "2I * K/2 = %lld bytes of one expert's weights must stay below 2^31",
+                (long long)2 * I * (K / 2));
+  if ((a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR) ||
+      (a2_scale_layout != W4A8_SCALE_ROW_MAJOR && a2_scale_layout != W4A8_SCALE_M_MAJOR))
+    return fail(W4A8_ERR_LAYOUT, "scale layouts %d, %d must be row-major (0) or M-major (1)", a_scale_layout,
+                a2_scale_layout);
+  if (!A_fp8_dev || !a_scales_dev || !B13_fp4_dev || !b13_scales_e8m0_dev || !expert_offsets_dev || !A2_fp8_dev ||
+      !a2_scales_dev)
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(A_fp8_dev, 16) || !aligned(B13_fp4_dev, 16) || !aligned(A2_fp8_dev, 16) ||
+      !aligned(a_scales_dev, 4) || !aligned(b13_scales_e8m0_dev, 4) || !aligned(expert_offsets_dev, 4) ||
+      !aligned(a2_scales_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "A, B13, A2 need 16-byte and scales/offsets 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B13_fp4_dev, b13_scales_e8m0_dev, expert_offsets_dev, nullptr,
+                      E, 2 * I, K, a_scale_layout, A2_fp8_dev, a2_scales_dev, I, a2_scale_layout};
+  hipError_t e = w4a8::launch_grouped_gemm_swiglu(args, d->grid, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_swiglu launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -5,6 +5,11 @@
 // (humming PR #129, "Results" command: FP8 E4M3 activations with fp32 scales
 // per 128 K, MXFP4 weights with E8M0 scales per 32 K, bf16 output.)
 //
+// The fused variant (grouped_gemm_kernel<true>) is the gate/up projection
+// with SwiGLU and the E4M3 requantization for the down projection in its
+// epilogue (swiglu.h): it writes A2 [R][I] codes and their scales instead of
+// the bf16 C.
+//
 // One persistent launch of 512 threads (8 waves) per CU.  Every workgroup
 // first runs the plan prologue (offsets into LDS, validity check, per-expert
 // tile counts of both classes), then the two phases over the tile plan:
@@ -21,6 +26,11 @@ constexpr int BLOCK = 512;
 static_assert(BLOCK == MF_THREADS, "both phases run on the same workgroup");
 constexpr int LDS_BYTES = P1_BYTES > P2_BYTES ? P1_BYTES : P2_BYTES;
 
+// FUSED: the gate/up GEMM with the SwiGLU + E4M3 requantization epilogue
+// (weights [E][2I][K/2], gate columns first); every expert with rows runs as
+// MFMA tiles of 256 output columns (the epilogue needs a row's 128-column
+// group inside one workgroup), so the streaming phase has no work.
+template <bool FUSED>
 __global__ void __launch_bounds__(BLOCK, 1)
 grouped_gemm_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -30,11 +40,12 @@ grouped_gemm_kernel(GemmArgs p) {
   __shared__ int s_info[3];
   __shared__ int s_eord[MAX_EXPERTS];
   __shared__ int s_rrc[5][4];
-  if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info)) return;
+  constexpr int smax = FUSED ? 0 : S_MAX;
+  if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info, smax)) return;
   const int R = uniform(s_off[p.E]);
 
   // phase 1: streaming items
-  {
+  if constexpr (!FUSED) {
     const int tiles = uniform(s_sbase[p.E]);
     const int nu = (p.N + 63) / 64;
     if (tiles > 0 && uniform(s_info[1]) == uniform(s_info[2]) &&
@@ -83,7 +94,8 @@ grouped_gemm_kernel(GemmArgs p) {
   {
     // MT <= R / 65 + E and NT <= 2^31 / 512 keep the item count in 32 bits
     const int MT = uniform(s_mbase[p.E]);
-    const int NT = (p.N + MF_BN - 1) / MF_BN;
+    constexpr int TILE_N = FUSED ? MF_BN / 2 : MF_BN;   // output columns per tile
+    const int NT = FUSED ? (p.I + TILE_N - 1) / TILE_N : (p.N + MF_BN - 1) / MF_BN;
     const int items = MT * NT;
     const int grid = gridDim.x;
     // this workgroup's round-r tile; invalid past its last one (item numbers
@@ -98,25 +110,30 @@ grouped_gemm_kernel(GemmArgs p) {
       const int j = mt - uniform(s_mbase[t.e]);
       const int base = uniform(s_off[t.e]);
       const int rows_e = uniform(s_off[t.e + 1]) - base;
-      const TileChoice tc = tile_rule(rows_e);
+      const TileChoice tc = tile_rule(rows_e, smax);
       t.row0 = base + j * tc.tile_m;
       t.rows = min(tc.tile_m, rows_e - j * tc.tile_m);
-      t.n0 = nt * MF_BN;
+      t.n0 = nt * TILE_N;
       t.valid = true;
       return t;
     };
     TileCoord t = tile_of(0);
-    for (int r = 0; t.valid; ++r) t = mfma_tile(p, lds, t, R, r > 0, [&]() { return tile_of(r + 1); });
+    for (int r = 0; t.valid; ++r) t = mfma_tile<FUSED>(p, lds, t, R, r > 0, [&]() { return tile_of(r + 1); });
   }
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3(grid), dim3(BLOCK), 0, stream, args);
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(BLOCK), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid), dim3(BLOCK), 0, stream, args);
   return hipGetLastError();
 }
 
 hipError_t grouped_gemm_occupancy(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, grouped_gemm_kernel, BLOCK, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, grouped_gemm_kernel<false>, BLOCK, 0);
 }
 
 }  // namespace w4a8

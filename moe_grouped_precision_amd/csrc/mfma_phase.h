@@ -6,6 +6,7 @@
 // re-read a real one and are never stored).  gfx950 only.
 #pragma once
 
+#include "swiglu.h"
 #include "w4a8_kernel.h"
 
 namespace w4a8 {
@@ -77,13 +78,25 @@ __device__ __forceinline__ void p2_read_x(const P2Lds& a, int mi, v4i& x0, v4i& 
   sa = ldsf(((mi & 1) ? a.sa1 : a.sa0) + mi * 16 * SC * 4);
 }
 
-// Coordinates of an MFMA tile: expert, first row, rows, first column.
+// Fused SwiGLU GEMM: weight column of tile-local column t (0 .. 511) of the
+// tile whose output columns start at c0.  Each wave's 64 columns are the
+// gate (first 32) and the up projection (last 32) of the same 32 output
+// columns c0 + 32 w .. c0 + 32 w + 31, so a lane holds gate and up of its
+// outputs in the same accumulator positions (blocks nb and nb + 2).
+// Output columns past I read the last one (never stored).
+__device__ __forceinline__ int fused_col(int c0, int t, int I) {
+  const int oc = min(c0 + (t >> 6) * 32 + (t & 31), I - 1);
+  return (t & 32) ? I + oc : oc;
+}
+
+// Coordinates of an MFMA tile: expert, first row, rows, first column
+// (an output column of A2 for the fused SwiGLU GEMM).
 struct TileCoord {
   int e, row0, rows, n0;
   bool valid;
 };
 
-template <int NMB>
+template <int NMB, bool FUSED = false>
 struct MfmaTile {
   const GemmArgs& p;
   uint8_t* lds;
@@ -105,11 +118,13 @@ struct MfmaTile {
     wn = wave;
     q = lane >> 4;
     r16 = lane & 15;
-    wvalid = uniform(n0 + wn * 64) < N;  // wave has columns inside N
+    // wave has columns inside N (inside I for the fused GEMM)
+    wvalid = FUSED ? uniform(n0 + wn * 32) < p.I : uniform(n0 + wn * 64) < N;
     // tile bases (uniform) and per-lane 32-bit offsets: K <= 2^20 keeps every
-    // in-tile offset below 2^32
+    // in-tile offset below 2^32 (the fused GEMM's offsets are from the
+    // expert's first column: N * K / 2 < 2^31 is checked on the host)
     xt = p.A + (size_t)row0 * K;
-    wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
+    wt = FUSED ? p.B + (size_t)e * N * (size_t)(K >> 1) : p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
 #pragma unroll
     for (int i = 0; i < P2_X_OPS; ++i) {
       const int r = (wave * P2_X_OPS + i) * 8 + (lane >> 3);
@@ -118,8 +133,12 @@ struct MfmaTile {
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int n = min(n0 + wn * 64 + nb * 16 + r16, N - 1);
-      wo[nb] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
+      if constexpr (FUSED) {
+        wo[nb] = (uint32_t)fused_col(n0, wn * 64 + nb * 16 + r16, p.I) * (uint32_t)(K >> 1) + q * 16;
+      } else {
+        const int n = min(n0 + wn * 64 + nb * 16 + r16, N - 1);
+        wo[nb] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
+      }
     }
     // LDS byte offsets of this lane's activation fragments within a slot
     xl0 = r16 * 128 + ((q ^ xkey(r16)) << 4);
@@ -150,7 +169,7 @@ struct MfmaTile {
     for (int i = 0; i < 4; ++i) {
       const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // rows [col] of SC words
       const int g = min(SC * c + ((lane & 3) ^ skey<SC>(col)), G - 1);
-      const int n = min(n0 + col, N - 1);
+      const int n = FUSED ? fused_col(n0, col, p.I) : min(n0 + col, N - 1);
       vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
               lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
     }
@@ -325,9 +344,11 @@ struct MfmaTile {
     // tile's first wait, which counts the newest operations, wait for more
     // than it needs)
     const TileCoord nt = next();
-    if (nt.valid) MfmaTile<1>(p, lds, nt.e, nt.row0, nt.rows, nt.n0, R).prologue_shared();
+    if (nt.valid) MfmaTile<1, FUSED>(p, lds, nt.e, nt.row0, nt.rows, nt.n0, R).prologue_shared();
 
-    if (wvalid) {
+    if constexpr (FUSED) {
+      fused_epilogue(acc);
+    } else if (wvalid) {
       // lane coordinates recomputed (opaque) rather than kept live through the K loop
       int t = threadIdx.x;
       asm volatile("" : "+v"(t));
@@ -349,20 +370,76 @@ struct MfmaTile {
     }
     return nt;
   }
+
+  // Fused SwiGLU epilogue: lane (q, i) holds, for row block mi, gate in
+  // acc[mi][0..1] and up in acc[mi][2..3] of output columns c0 + 32 w +
+  // 16 j + 4 q .. +3 (j = 0, 1) of row 16 mi + i.  h = silu(gate) * up
+  // replaces the gate accumulators; each row's amax over the wave's 32
+  // columns goes through LDS to the four waves of its 128-column group
+  // (waves 0-3: c0 .. c0+127, waves 4-7: c0+128 ..).  The LDS words used
+  // are in ring slots 4-5, which the next tile's first loads (slots 0-3,
+  // scale chunk 0) leave alone and its first K pair refills only after its
+  // first barrier.  Every wave reaches the barrier, with columns or not.
+  __device__ __forceinline__ void fused_epilogue(v4f (&acc)[8][4]) {
+    float* s_amax = reinterpret_cast<float*>(lds + 4 * P2_XSLOT);  // [8 waves][128 rows]
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int w = t >> 6, eq = (t >> 4) & 3, er = t & 15;
+    if (wvalid) {
+#pragma unroll
+      for (int mi = 0; mi < NMB; ++mi) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[mi][j][c] = swiglu_f32(acc[mi][j][c], acc[mi][j + 2][c]);
+            m = fmaxf(m, fabsf(acc[mi][j][c]));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (eq == 0) s_amax[w * 128 + mi * 16 + er] = m;
+      }
+    }
+    __syncthreads();
+    if (wvalid) {
+      const int I = p.I, G2 = I >> 7;
+      const int grp = (n0 >> 7) + (w >> 2);          // 128-column group of this wave's columns
+      const float* am = s_amax + (w & 4) * 128;      // the group's four waves
+#pragma unroll
+      for (int mi = 0; mi < NMB; ++mi) {
+        const int m = mi * 16 + er;
+        if (m < rows) {
+          const float amax = fmaxf(fmaxf(am[m], am[128 + m]), fmaxf(am[256 + m], am[384 + m]));
+          const float s = e4m3_group_scale(amax);
+          const float inv = __fdiv_rn(1.0f, s);
+          const size_t row = (size_t)row0 + m;
+          uint8_t* arow = p.A2 + row * I + n0 + w * 32 + eq * 4;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const v4f h = acc[mi][j];
+            *reinterpret_cast<uint32_t*>(arow + 16 * j) = e4m3x4(h[0], h[1], h[2], h[3], inv);
+          }
+          if ((w & 3) == 0 && eq == 0)
+            p.SA2[p.layout2 ? (size_t)grp * R + row : row * G2 + grp] = s;
+        }
+      }
+    }
+  }
 };
 
-template <class Next>
+template <bool FUSED = false, class Next>
 __device__ __forceinline__ TileCoord mfma_tile(const GemmArgs& p, uint8_t* lds, const TileCoord& t, int R,
                                                bool shared_ready, Next next) {
   switch ((t.rows + 15) >> 4) {
-    case 1: return MfmaTile<1>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 2: return MfmaTile<2>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 3: return MfmaTile<3>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 4: return MfmaTile<4>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 5: return MfmaTile<5>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 6: return MfmaTile<6>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    case 7: return MfmaTile<7>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
-    default: return MfmaTile<8>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 1: return MfmaTile<1, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 2: return MfmaTile<2, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 3: return MfmaTile<3, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 4: return MfmaTile<4, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 5: return MfmaTile<5, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 6: return MfmaTile<6, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    case 7: return MfmaTile<7, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
+    default: return MfmaTile<8, FUSED>(p, lds, t.e, t.row0, t.rows, t.n0, R).run(shared_ready, next);
   }
 }
 

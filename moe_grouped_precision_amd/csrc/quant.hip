@@ -19,6 +19,7 @@
 // TransformerEngine PR #3459 (description: register-only rowwise cast, no
 // shared memory or barrier), nothing is staged; unlike them the scale is the
 // fp32 amax/448 of 128 elements, not an E8M0 exponent of 32.
+#include "swiglu.h"
 #include "w4a8_launch.h"
 
 #include <hip/hip_runtime.h>
@@ -99,32 +100,11 @@ quant_gather_kernel(const uint16_t* __restrict__ x, int K, const int32_t* __rest
   }
 }
 
-// h = silu(g) * u = g / (1 + e^-g) * u in fp32 with the hardware exponential
-// and reciprocal: e^-g = 2^n * 2^(r log2 e) with n = rint(-g log2 e) and
-// r = -g - n ln2 by two fused multiply-adds (ln2 split into its fp32 value
-// and the fp32 value of the rest), so the argument of v_exp_f32 lies in
-// [-1/2, 1/2] and carries no error from the size of g; 2^n by an exact
-// ldexp.  -g is clamped to [-104, 104]: above about 88.7 e^-g overflows to
-// inf and silu to -0 (its magnitude is below 2^-120 there), below -104 it
-// underflows and silu is g.  The result is within about five fp32 units in
-// the last place of silu(g) * u (exp, reciprocal, three roundings).
-constexpr float kLog2e = 1.44269502162933349609375f;   // fp32(log2 e)
-constexpr float kLn2Hi = 0.693147182464599609375f;     // fp32(ln 2)
-constexpr float kLn2Lo = -1.9046542121259336e-09f;     // fp32(ln 2 - kLn2Hi)
-__device__ __forceinline__ float swiglu_f32(float g, float u) {
-  const float x = fminf(fmaxf(-g, -104.0f), 104.0f);
-  const float n = rintf(x * kLog2e);
-  const float r = fmaf(-n, kLn2Lo, fmaf(-n, kLn2Hi, x));
-  const float e = ldexpf(__builtin_amdgcn_exp2f(r * kLog2e), (int)n);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
-// SwiGLU of the gate/up output and its E4M3 requantization: one workgroup
-// per row; 8 lanes per 128-column group, 16 columns of gate (columns 0 ..
-// I-1) and the same 16 of up (columns I .. 2I-1) per lane; h as above, then
-// per group s = amax / 448 (IEEE division; 1 for an all-zero group), v =
-// clip(h * (1/s), +-448) and the E4M3FN code of v by the hardware conversion
-// (v_cvt_pk_fp8_f32: round to nearest even, OCP E4M3 on gfx950).
+// SwiGLU of the gate/up output and its E4M3 requantization (swiglu.h): one
+// workgroup per row; 8 lanes per 128-column group, 16 columns of gate
+// (columns 0 .. I-1) and the same 16 of up (columns I .. 2I-1) per lane;
+// per group s = amax / 448, v = clip(h * (1/s), +-448) and its E4M3FN code
+// by the hardware conversion.
 __global__ void __launch_bounds__(512)
 swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __restrict__ A, float* __restrict__ SA,
                     int layout) {
@@ -156,18 +136,12 @@ swiglu_quant_kernel(const uint16_t* __restrict__ C, int R, int I, uint8_t* __res
     m = fmaxf(m, __shfl_xor(m, 1, 8));
     m = fmaxf(m, __shfl_xor(m, 2, 8));
     m = fmaxf(m, __shfl_xor(m, 4, 8));
-    const float s = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+    const float s = e4m3_group_scale(m);
     const float inv = __fdiv_rn(1.0f, s);
-    int c[4];
+    uint32_t c[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float y[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(h[4 * i + j] * inv, -448.0f), 448.0f);
-      c[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      c[i] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c[i], true);
-    }
-    const v4u out = {(uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]};
+    for (int i = 0; i < 4; ++i) c[i] = e4m3x4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3], inv);
+    const v4u out = {c[0], c[1], c[2], c[3]};
     __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(A + (size_t)r * I + g * 128 + lane8 * 16));
     if (lane8 == 0) SA[layout ? (size_t)g * R + r : (size_t)r * G + g] = s;
   }

@@ -46,11 +46,13 @@ struct TileChoice {
   int n_m;
 };
 
-__host__ __device__ inline TileChoice tile_rule(int rows) {
+// smax = S_MAX for the plain GEMM; the fused SwiGLU GEMM, whose epilogue
+// lives in the MFMA phase only, passes 0 (every expert with rows is MFMA).
+__host__ __device__ inline TileChoice tile_rule(int rows, int smax = S_MAX) {
   TileChoice t;
   if (rows <= 0) {
     t.cls = CLASS_NONE; t.tile_m = 0; t.n_m = 0;
-  } else if (rows <= S_MAX) {
+  } else if (rows <= smax) {
     t.cls = CLASS_STREAM; t.tile_m = (rows + GRAN - 1) / GRAN * GRAN; t.n_m = 1;
   } else {
     t.cls = CLASS_MFMA;
@@ -134,7 +136,7 @@ __device__ inline int wave_max_nonneg(int x) {
 // Returns false (uniformly across the block) if the offsets are invalid.
 // ---------------------------------------------------------------------------
 __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E, int* s_off,
-                                     int* s_sbase, int* s_mbase, int* s_info) {
+                                     int* s_sbase, int* s_mbase, int* s_info, int smax = S_MAX) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 64) / 64;  // offsets per lane, so that 64 * per > E
@@ -149,7 +151,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
         if (e < E) {
           const int b = offsets[e + 1];
           bad |= b < a;
-          const TileChoice t = tile_rule(b - a);
+          const TileChoice t = tile_rule(b - a, smax);
           if (t.cls == CLASS_STREAM) {
             ls += t.n_m;
             mb = max(mb, t.tile_m / GRAN);
@@ -170,7 +172,7 @@ __device__ inline bool plan_prologue(const int32_t* __restrict__ offsets, int E,
         if (e < E) {
           s_sbase[e] = rs;
           s_mbase[e] = rm;
-          const TileChoice t = tile_rule(s_off[e + 1] - s_off[e]);
+          const TileChoice t = tile_rule(s_off[e + 1] - s_off[e], smax);
           rs += t.cls == CLASS_STREAM ? t.n_m : 0;
           rm += t.cls == CLASS_MFMA ? t.n_m : 0;
         }

@@ -13,8 +13,12 @@ struct GemmArgs {
   const uint8_t* B;        // [E][N][K/2] packed E2M1
   const uint8_t* SB;       // [E][N][K/32] E8M0
   const int32_t* offsets;  // [E+1]
-  uint16_t* C;             // [R][N] bf16 bits
+  uint16_t* C;             // [R][N] bf16 bits (the plain GEMM)
   int E, N, K, layout;     // layout 0 row-major, 1 M-major
+  // fused SwiGLU epilogue (N = 2 I weight columns: gate 0 .. I-1, up I .. 2I-1)
+  uint8_t* A2;             // [R][I] E4M3 codes of silu(gate) * up
+  float* SA2;              // per (row, 128 columns of A2), layout2
+  int I, layout2;
 };
 
 // Route prep: the workgroup holds ROUTE_MAX_WAVES waves, W of which rank
@@ -30,6 +34,7 @@ hipError_t launch_route_prep(const int32_t* ids, int n, int E, int W, int32_t* c
 hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int max_tiles,
                        hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream);
+hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t grouped_gemm_occupancy(int* blocks);
 hipError_t launch_combine(const uint16_t* C, int R, int N, const int32_t* row_of_slot, const float* weights, int T,
                           int top_k, uint16_t* out, hipStream_t stream);

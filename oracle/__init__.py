@@ -46,4 +46,4 @@ from .plan import PLAN_PARAMS, plan_ref, tile_rule  # noqa: F401
 from .route import route_ref  # noqa: F401
 from .quant import bf16_bits_to_f32, e4m3_encode_rne, quantize_gather, quantize_tokens  # noqa: F401
 from .combine import combine_ref  # noqa: F401
-from .swiglu import check_swiglu_quant, silu_f64, swiglu_f64, swiglu_quant_f64  # noqa: F401
+from .swiglu import check_h_quant, check_swiglu_quant, h_quant_f64, silu_f64, swiglu_f64, swiglu_quant_f64  # noqa: F401

@@ -27,10 +27,11 @@ fp64 ones:
     overflows fp32 (g below about -88.7, where silu(g) rounds to -0 although
     its magnitude is below 2^-120, or where the reciprocal of 1 + e^-g is
     subnormal).
-  * the scale s' of a group is admissible when |s' - amax/448| <= S_REL *
-    amax/448 + H_ABS * max|u| / 448 (amax of admissible h' can differ from
-    the fp64 amax by no more than that), or when s' = 1 and every h of the
-    group is within H_ABS * |u| of zero.
+  * the scale s' of a group is admissible when |s' - amax/448| <=
+    max(slack)/448 + 2^-23 * amax/448, the slack of an element being the
+    bound on |h' - h| above (amax of admissible h' can differ from the fp64
+    amax by no more than the largest slack; the division by 448 rounds), or
+    when s' = 1 and every h of the group is within its slack of zero.
   * a code is admissible when its value is the E4M3 round-to-nearest-even of
     clip(v, +-448) for some v with |v - h/s'| <= (H_REL * |h| + H_ABS * |u|)
     / s' + Q_REL * |h/s'| (the quotient by s' itself rounded in fp32).
@@ -48,7 +49,6 @@ from .quant import E4M3_MAX, bf16_bits_to_f32, e4m3_encode_rne
 
 H_REL = 2.0 ** -20
 H_ABS = 2.0 ** -118
-S_REL = 2.0 ** -19
 Q_REL = 2.0 ** -21
 
 
@@ -79,6 +79,13 @@ def swiglu_quant_f64(C_bits: np.ndarray, layout: int):
     `layout`: row-major [R][I/128] or M-major [I/128][R]), the definition
     evaluated in fp64: s = amax/448 (1 if amax = 0), code = RNE(clip(h/s))."""
     g, u, R, I = _split(C_bits)
+    return h_quant_f64(g, u, layout)
+
+
+def h_quant_f64(g: np.ndarray, u: np.ndarray, layout: int):
+    """The same from fp64 gate and up values g, u [R][I] (the fused GEMM's
+    definition: the exact GEMM outputs, not rounded to bf16)."""
+    R, I = g.shape
     h = swiglu_f64(g, u)
     G = I // 128
     hg = h.reshape(R, G, 128)
@@ -92,29 +99,50 @@ def swiglu_quant_f64(C_bits: np.ndarray, layout: int):
 
 def check_swiglu_quant(C_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, layout: int) -> dict:
     """Admissibility of a result (codes uint8 [R][I], fp32 scales flat in
-    `layout`) against the fp64 definition, with the bounds of the module
-    docstring.  Returns counts: bad_scales, bad_codes, nan (codes or scales
-    that are NaN), ambiguous (elements for which more than one code value is
+    `layout`) of the SwiGLU step applied to the bf16 gate/up output C_bits,
+    against the fp64 definition, with the bounds of the module docstring."""
+    g, u, R, I = _split(C_bits)
+    return check_h_quant(g, u, codes, scales, layout)
+
+
+def check_h_quant(g: np.ndarray, u: np.ndarray, codes: np.ndarray, scales: np.ndarray, layout: int,
+                  g_slack: np.ndarray | None = None, u_slack: np.ndarray | None = None) -> dict:
+    """Admissibility of E4M3 codes and fp32 scales of h = silu(g) * u for
+    fp64 gate and up values g, u [R][I].  g_slack / u_slack (same shape, or
+    None for 0) widen the check for inputs that are themselves computed with
+    a bounded error (the fused GEMM's fp32 accumulators): any g' within
+    g_slack of g and u' within u_slack of u may have been used, and since
+    |silu'| <= 1.1 everywhere, |silu(g') u' - silu(g) u| <= 1.1 g_slack
+    (|u| + u_slack) + |silu(g)| u_slack is added to each element's slack.
+    Returns counts: bad_scales, bad_codes, nan (codes or scales that are
+    NaN), ambiguous (elements for which more than one code value is
     admissible), elements, and max_scale_rel (the largest relative distance
     of an accepted scale from amax/448, over groups not within the floor of
     zero)."""
-    g, u, R, I = _split(C_bits)
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    R, I = g.shape
     G = I // 128
     codes = np.asarray(codes, dtype=np.uint8).reshape(R, I)
     s_in = np.asarray(scales, dtype=np.float32).reshape(-1).astype(np.float64)
     if s_in.size != R * G:
         raise ValueError("scales must hold R * I/128 values")
     sg = s_in.reshape(R, G) if layout == 0 else s_in.reshape(G, R).T
-    h = swiglu_f64(g, u)
+    sil = silu_f64(g)
+    h = sil * u
     au = np.abs(u)
     slack = H_REL * np.abs(h) + H_ABS * au                     # per element
+    if g_slack is not None or u_slack is not None:
+        gs = np.zeros_like(g) if g_slack is None else np.asarray(g_slack, dtype=np.float64)
+        us = np.zeros_like(u) if u_slack is None else np.asarray(u_slack, dtype=np.float64)
+        slack = slack + 1.1 * gs * (au + us) + np.abs(sil) * us
     hg = np.abs(h).reshape(R, G, 128)
     amax = hg.max(axis=2)
-    umax = au.reshape(R, G, 128).max(axis=2)
     ref = amax / E4M3_MAX
-    tiny = np.all(hg <= (H_ABS * au).reshape(R, G, 128), axis=2)  # the group may read as all zero
+    sl_g = slack.reshape(R, G, 128)
+    tiny = np.all(hg <= sl_g, axis=2)                          # the group may read as all zero
     nan_s = ~np.isfinite(sg) | (sg <= 0)
-    ok_s = (np.abs(sg - ref) <= S_REL * ref + H_ABS * umax / E4M3_MAX) | (tiny & (sg == 1.0))
+    ok_s = (np.abs(sg - ref) <= sl_g.max(axis=2) / E4M3_MAX + 2.0 ** -23 * ref) | (tiny & (sg == 1.0))
     ok_s &= ~nan_s
     sgf = np.where(nan_s, 1.0, sg)
     s_el = np.repeat(sgf, 128, axis=1)

@@ -168,6 +168,26 @@ def test_swiglu_quant_host_validation(lib):
     assert lib.w4a8_last_error() != b""
 
 
+def test_grouped_gemm_swiglu_host_validation(lib):
+    f = lib.w4a8_grouped_gemm_swiglu
+    ok = (P16, P16, 0, P16, P16, P16, 8, 256, 512, P16, P16, 0, NUL)
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=0) == 2                      # E = 0
+    assert call(a7=200) == 2                    # I % 128
+    assert call(a7=0) == 2                      # I = 0
+    assert call(a8=500) == 2                    # K % 128
+    assert call(a7=1 << 16, a8=1 << 16) == 2    # one expert's weights past 2^31 bytes
+    assert call(a2=2) == 3 and call(a11=2) == 3  # bad layouts
+    assert call(a9=NUL) == 1 and call(a10=NUL) == 1 and call(a3=NUL) == 1
+    assert call(a9=P4) == 4 and call(a3=P4) == 4 and call(a0=P4) == 4
+    assert lib.w4a8_last_error() != b""
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():

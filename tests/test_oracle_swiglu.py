@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 from scipy.special import expit
 
-from oracle import check_swiglu_quant, e4m3_table, silu_f64, swiglu_f64, swiglu_quant_f64
+from oracle import (check_h_quant, check_swiglu_quant, e4m3_table, h_quant_f64, silu_f64, swiglu_f64,
+                    swiglu_quant_f64)
 from oracle.quant import e4m3_encode_rne
 
 
@@ -167,3 +168,21 @@ def test_check_rejects_planted_mistakes(mistake):
         codes[4, 3] = 0x7F
     r = check_swiglu_quant(bits, codes, s, layout)
     assert r["bad_codes"] + r["bad_scales"] > 0, r
+
+
+def test_h_quant_matches_bf16_path_and_slack_widens():
+    """h_quant_f64 on the bf16 values equals swiglu_quant_f64; g_slack /
+    u_slack accept results computed from perturbed inputs that are rejected
+    without them."""
+    bits = _case(R=16, I=256, seed=9)
+    g, u = _f(bits)[:, :256], _f(bits)[:, 256:]
+    c0, s0 = swiglu_quant_f64(bits, 0)
+    c1, s1 = h_quant_f64(g, u, 0)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    gp, up = g * (1 + 3e-4), u * (1 - 3e-4)           # inputs off by 3e-4 relative
+    cp, sp = h_quant_f64(gp, up, 0)
+    r = check_h_quant(g, u, cp, sp.astype(np.float32), 0)
+    assert r["bad_codes"] + r["bad_scales"] > 0
+    r = check_h_quant(g, u, cp, sp.astype(np.float32), 0, g_slack=3e-4 * np.abs(g) * 1.001,
+                      u_slack=3e-4 * np.abs(u) * 1.001)
+    assert r["bad_codes"] == 0 and r["bad_scales"] == 0, r
