@@ -435,6 +435,39 @@ def measure_gemm_wide_pool(reps=5):
     return out
 
 
+def measure_gemm_planned_wide_pool(reps=5, E=6144):
+    """The grouped GEMM over the largest shared pool MoonEP PR #38 times (6144
+    experts, 16384 tokens at top-8, uniform routing) at the benchmark's
+    gate/up expert shape N=4096, K=6144, beyond the plain GEMM's per-expert
+    tables: w4a8_plan once, then w4a8_grouped_gemm_planned (timed).  Random
+    codes drawn on the GPU; about 82 GB of weights, read once per launch."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    T, k, N, K = 16384, 8, 4096, 6144
+    ids = synth.make_wide_routing(T, E, k, seed=E).to("cuda")
+    counts, off, _ = w4a8.route_prep(ids, E)
+    counts = counts.cpu().numpy()
+    R = int(counts.sum())
+    A, SA, B, SB = synth.wide_pool_codes(counts.tolist(), N, K, seed=13)
+    C = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    plan = w4a8.plan(off, E, N, K, max_total_rows=R)
+    ms_plan = time_launches(lambda i: w4a8.plan(off, E, N, K, out=plan), 10)
+    ms = time_launches(lambda i: w4a8.grouped_gemm_planned(A, SA, 0, B, SB, off, plan, out=C), reps, warmup=2)
+    hit = int((counts > 0).sum())
+    flops = 2.0 * R * N * K
+    out = _hbm_result(f"{T} tokens x top-{k} over {E} experts ({hit} with rows, at most {int(counts.max())} "
+                      f"rows), N={N} K={K}, uniform routing, row-major scales, plan built once", ms,
+                      algorithmic_bytes(counts, E, N, K), flop=flops,
+                      tflops=round(flops / (statistics.median(ms) * 1e-3) / 1e12, 1),
+                      plan_us_median=round(statistics.median(ms_plan) * 1e3, 2))
+    del A, SA, B, SB, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_gemm_swiglu(reps=10):
     """The gate/up GEMM with the SwiGLU + E4M3 requantization epilogue
     (w4a8_grouped_gemm_swiglu) on the large prefill gate/up workload (16384
@@ -542,7 +575,8 @@ def main():
         extras = {"grouped_gemm_swiglu": measure_gemm_swiglu(),
                   "quantize_gather": measure_quantize_gather(), "swiglu_quant": measure_swiglu_quant(),
                   "combine": measure_combine(), "route_prep_wide_pool": measure_route_prep_wide(),
-                  "grouped_gemm_wide_pool": measure_gemm_wide_pool()}
+                  "grouped_gemm_wide_pool": measure_gemm_wide_pool(),
+                  "grouped_gemm_planned_wide_pool": measure_gemm_planned_wide_pool()}
 
     # the headline workload: W untimed steps, then K timed steps
     log(f"{name} layout {layout}: generating")

@@ -243,6 +243,38 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
                       uint16_t* C_bf16_dev, void* stream);
 
 /*
+ * w4a8_grouped_gemm_planned -- the grouped W4A8 GEMM of w4a8_grouped_gemm,
+ * run over a tile list built beforehand instead of one the kernel derives
+ * from the offsets.  The per-expert tables of w4a8_grouped_gemm live in LDS
+ * and stop at W4A8_MAX_EXPERTS; this entry point keeps none, so it serves
+ * the shared expert pools of thousands of experts that MoonEP PR #38
+ * (background section) plans for, up to W4A8_MAX_PREP_EXPERTS.  One plan
+ * serves every GEMM over the same offsets (gate/up and down of a layer).
+ *
+ * plan_dev, plan_bytes  a plan in w4a8_plan's format (header, then
+ *                    {expert, first row, rows, tile_m | class << 16} per
+ *                    m-tile, streaming tiles first), normally w4a8_plan's
+ *                    output for the same offsets, E and N; caller-owned,
+ *                    read only.  4-byte aligned.  Other rules may be run
+ *                    through it as long as every streaming tile (class 1)
+ *                    holds 1 .. S_MAX rows and every MFMA tile (class 2)
+ *                    1 .. T_MAX rows (w4a8_plan_params).
+ * Every tile is checked against the offsets before use: a tile whose rows
+ * are not inside its expert's rows and inside [0, R) is skipped (its rows
+ * are then not written), so no plan makes the kernel touch memory outside
+ * A, a_scales, B, b_scales and C.  A plan whose status word is not 0 makes
+ * the kernel write nothing.  Streaming tiles are dealt as items of up to
+ * three 64-column units, MFMA tiles as 512-column items.  The other
+ * arguments, layouts, numerics and limits are those of w4a8_grouped_gemm,
+ * except 1 <= E <= W4A8_MAX_PREP_EXPERTS.  plan_bytes below the header ->
+ * W4A8_ERR_CAPACITY.
+ */
+int w4a8_grouped_gemm_planned(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                              const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                              const int32_t* expert_offsets_dev, int E, int N, int K, const void* plan_dev,
+                              size_t plan_bytes, uint16_t* C_bf16_dev, void* stream);
+
+/*
  * w4a8_grouped_gemm_swiglu -- the gate/up projection with the step between
  * the two projections fused into its epilogue (humming PR #129 "Results"
  * and PR #58 "H200 performance" time gate/up and down as a pair): the

@@ -42,6 +42,8 @@ def _declare(lib):
     lib.w4a8_plan.restype = i32
     lib.w4a8_grouped_gemm.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.w4a8_grouped_gemm.restype = i32
+    lib.w4a8_grouped_gemm_planned.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp, vp]
+    lib.w4a8_grouped_gemm_planned.restype = i32
     lib.w4a8_grouped_gemm_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
     lib.w4a8_grouped_gemm_swiglu.restype = i32
     lib.w4a8_swiglu_quant.argtypes = [vp, i32, i32, vp, vp, i32, vp]
@@ -191,6 +193,37 @@ def grouped_gemm(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor
     _check("w4a8_grouped_gemm", lib.w4a8_grouped_gemm(
         _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
         _ptr(out), _stream()))
+    return out
+
+
+def grouped_gemm_planned(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor, SB: torch.Tensor,
+                         expert_offsets: torch.Tensor, plan: torch.Tensor,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[R, N] (bf16) of the grouped W4A8 GEMM over a tile list `plan` (int32,
+    w4a8_plan's format, e.g. the output of plan()); the rest as grouped_gemm."""
+    lib = load()
+    if A.dim() != 2 or B.dim() != 3 or SB.dim() != 3:
+        raise ValueError("A must be [R, K], B [E, N, K/2], SB [E, N, K/32]")
+    R, K = A.shape
+    E, N, Kh = B.shape
+    if Kh * 2 != K or SB.shape != (E, N, K // 32):
+        raise ValueError("inconsistent K between A, B and SB")
+    _need(A, "A", torch.uint8)
+    _need(SA, "a_scales", torch.float32, R * (K // 128))
+    _need(B, "B", torch.uint8)
+    _need(SB, "b_scales", torch.uint8)
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    _need(plan, "plan", torch.int32)
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=A.device)
+    if out.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("out must be bfloat16 (or 16-bit integer bits)")
+    _need(out, "out", out.dtype, R * N)
+    if R == 0:
+        return out
+    _check("w4a8_grouped_gemm_planned", lib.w4a8_grouped_gemm_planned(
+        _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K, _ptr(plan),
+        plan.numel() * 4, _ptr(out), _stream()))
     return out
 
 

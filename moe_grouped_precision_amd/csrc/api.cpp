@@ -185,9 +185,39 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
   st = device_info(&d);
   if (st != W4A8_OK) return st;
   w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev,
-                      C_bf16_dev, E, N, K, a_scale_layout, nullptr, nullptr, 0, 0};
+                      C_bf16_dev, E, N, K, a_scale_layout, nullptr, nullptr, 0, 0, nullptr, 0};
   hipError_t e = w4a8::launch_grouped_gemm(args, d->grid, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_grouped_gemm_planned(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                              const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                              const int32_t* expert_offsets_dev, int E, int N, int K, const void* plan_dev,
+                              size_t plan_bytes, uint16_t* C_bf16_dev, void* stream) {
+  int st = check_gemm_shape(E, N, K, W4A8_MAX_PREP_EXPERTS);
+  if (st != W4A8_OK) return st;
+  if (a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR)
+    return fail(W4A8_ERR_LAYOUT, "a_scale_layout=%d is neither row-major (0) nor M-major (1)", a_scale_layout);
+  if (!A_fp8_dev || !a_scales_dev || !B_fp4_dev || !b_scales_e8m0_dev || !expert_offsets_dev || !plan_dev ||
+      !C_bf16_dev)
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(A_fp8_dev, 16) || !aligned(B_fp4_dev, 16) || !aligned(C_bf16_dev, 16) ||
+      !aligned(a_scales_dev, 4) || !aligned(b_scales_e8m0_dev, 4) || !aligned(expert_offsets_dev, 4) ||
+      !aligned(plan_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "A, B, C need 16-byte and scales/offsets/plan 4-byte alignment");
+  const size_t words = plan_bytes / sizeof(int32_t);
+  if (words < (size_t)w4a8::PLAN_HEADER_WORDS)
+    return fail(W4A8_ERR_CAPACITY, "plan buffer of %zu bytes cannot hold the header", plan_bytes);
+  size_t max_tiles = (words - w4a8::PLAN_HEADER_WORDS) / w4a8::PLAN_TILE_WORDS;
+  if (max_tiles > (size_t)0x7fffffff) max_tiles = 0x7fffffff;
+  const DeviceInfo* d = nullptr;
+  st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev, C_bf16_dev,
+                      E, N, K, a_scale_layout, nullptr, nullptr, 0, 0, (const int32_t*)plan_dev, (int)max_tiles};
+  hipError_t e = w4a8::launch_grouped_gemm_planned(args, d->grid, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_planned launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -217,7 +247,7 @@ int w4a8_grouped_gemm_swiglu(const uint8_t* A_fp8_dev, const float* a_scales_dev
   st = device_info(&d);
   if (st != W4A8_OK) return st;
   w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B13_fp4_dev, b13_scales_e8m0_dev, expert_offsets_dev, nullptr,
-                      E, 2 * I, K, a_scale_layout, A2_fp8_dev, a2_scales_dev, I, a2_scale_layout};
+                      E, 2 * I, K, a_scale_layout, A2_fp8_dev, a2_scales_dev, I, a2_scale_layout, nullptr, 0};
   hipError_t e = w4a8::launch_grouped_gemm_swiglu(args, d->grid, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_swiglu launch: %s", hipGetErrorString(e));
   return ok();

@@ -122,6 +122,86 @@ grouped_gemm_kernel(GemmArgs p) {
   }
 }
 
+// The grouped GEMM driven by a tile list built beforehand (w4a8_plan's
+// format: header, then {expert, first row, rows, tile_m | class << 16} per
+// m-tile, streaming tiles first): no per-expert tables in LDS, so the
+// number of experts is bounded only by the plan (the shared expert pools of
+// thousands of experts of MoonEP PR #38, background section), and any rule
+// that respects the two phases' limits can be run (a streaming tile holds at
+// most S_MAX rows, an MFMA tile at most T_MAX).  Every tile is checked
+// against the offsets before use -- its rows inside its expert's rows and
+// inside [0, R) -- and skipped otherwise, so no plan can make the kernel
+// touch rows outside A, a_scales and C.  A plan whose status word is not 0
+// makes the kernel write nothing.
+__device__ __forceinline__ bool planned_tile(const GemmArgs& p, int R, int idx, int cls, int max_rows, int* e,
+                                             int* row0, int* rows) {
+  const int32_t* t = p.plan + PLAN_HEADER_WORDS + (size_t)idx * PLAN_TILE_WORDS;
+  *e = uniform(t[0]);
+  *row0 = uniform(t[1]);
+  *rows = uniform(t[2]);
+  const int tc = uniform(t[3]);
+  if ((tc >> 16) != cls || *e < 0 || *e >= p.E || *rows < 1 || *rows > max_rows) return false;
+  const int lo = uniform(p.offsets[*e]), hi = uniform(p.offsets[*e + 1]);
+  return *row0 >= lo && *row0 >= 0 && (long long)*row0 + *rows <= hi && (long long)*row0 + *rows <= R;
+}
+
+__global__ void __launch_bounds__(BLOCK, 1)
+grouped_gemm_planned_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  const int R = uniform(p.offsets[p.E]);
+  if (uniform(p.plan[0]) != PLAN_OK || uniform(p.offsets[0]) != 0) return;
+  const int ns = max(0, min(uniform(p.plan[2]), p.max_tiles));
+  const int nm = max(0, min(uniform(p.plan[3]), p.max_tiles - ns));
+  const int G = gridDim.x;
+
+  // phase 1: streaming tiles, items of (up to) three 64-column units dealt
+  // round-robin in a snake order
+  {
+    const int nu = (p.N + 63) / 64;
+    constexpr int W = P1_RANGE_MAXNBW;
+    const int ipt = (nu + W - 1) / W;
+    const long long items = (long long)ns * ipt;
+    for (long long r = 0;; ++r) {
+      const long long it = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+      if (it >= items) break;
+      const int t = (int)(it / ipt), c = (int)(it - (long long)t * ipt);
+      int e, row0, rows;
+      if (!planned_tile(p, R, t, CLASS_STREAM, S_MAX, &e, &row0, &rows)) continue;
+      stream_item(p, lds, e, row0, rows, c * W * 64, min(W, nu - c * W), R);
+    }
+  }
+
+  // phase 2: MFMA tiles, dealt as in grouped_gemm_kernel; tiles that fail
+  // the check are passed over
+  {
+    const int NT = (p.N + MF_BN - 1) / MF_BN;
+    const int items = nm * NT;  // nm <= R / 65 + E keeps it in 32 bits
+    int r = 0;
+    auto next_tile = [&]() -> TileCoord {
+      for (;; ++r) {
+        TileCoord t{0, 0, 0, 0, false};
+        const int L = xcd_item(r, blockIdx.x, G);
+        if (L >= items) return t;
+        int mt, nt;
+        item_tile(L, nm, NT, &mt, &nt);
+        if (planned_tile(p, R, ns + mt, CLASS_MFMA, T_MAX, &t.e, &t.row0, &t.rows)) {
+          t.n0 = nt * MF_BN;
+          t.valid = true;
+          ++r;
+          return t;
+        }
+      }
+    };
+    TileCoord t = next_tile();
+    for (bool ready = false; t.valid; ready = true) t = mfma_tile<false>(p, lds, t, R, ready, next_tile);
+  }
+}
+
+hipError_t launch_grouped_gemm_planned(const GemmArgs& args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_gemm_planned_kernel, dim3(grid), dim3(BLOCK), 0, stream, args);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid), dim3(BLOCK), 0, stream, args);
   return hipGetLastError();

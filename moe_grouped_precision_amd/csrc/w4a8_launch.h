@@ -19,6 +19,9 @@ struct GemmArgs {
   uint8_t* A2;             // [R][I] E4M3 codes of silu(gate) * up
   float* SA2;              // per (row, 128 columns of A2), layout2
   int I, layout2;
+  // planned GEMM: a tile list in w4a8_plan's format holding at most max_tiles tiles
+  const int32_t* plan;
+  int max_tiles;
 };
 
 // Route prep: the workgroup holds ROUTE_MAX_WAVES waves, W of which rank
@@ -35,6 +38,7 @@ hipError_t launch_plan(const int32_t* offsets, int E, int N, int32_t* plan, int 
                        hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t launch_grouped_gemm_swiglu(const GemmArgs& args, int grid, hipStream_t stream);
+hipError_t launch_grouped_gemm_planned(const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t grouped_gemm_occupancy(int* blocks);
 hipError_t launch_combine(const uint16_t* C, int R, int N, const int32_t* row_of_slot, const float* weights, int T,
                           int top_k, uint16_t* out, hipStream_t stream);

@@ -168,6 +168,24 @@ def test_swiglu_quant_host_validation(lib):
     assert lib.w4a8_last_error() != b""
 
 
+def test_grouped_gemm_planned_host_validation(lib):
+    f = lib.w4a8_grouped_gemm_planned
+    ok = [P16, P16, 0, P16, P16, P16, 8, 256, 512, P16, 1024, P16, NUL]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=0) == 2 and call(a6=65537) == 2       # E outside [1, 65536]
+    assert call(a8=500) == 2 and call(a7=48) == 2        # K % 128, N % 32
+    assert call(a2=2) == 3                               # bad layout
+    assert call(a9=NUL) == 1 and call(a11=NUL) == 1      # null plan, null C
+    assert call(a9=ctypes.c_void_p((1 << 20) + 2)) == 4  # misaligned plan
+    assert call(a10=16) == 5                             # plan buffer below the header
+    assert lib.w4a8_last_error() != b""
+
+
 def test_grouped_gemm_swiglu_host_validation(lib):
     f = lib.w4a8_grouped_gemm_swiglu
     ok = (P16, P16, 0, P16, P16, P16, 8, 256, 512, P16, P16, 0, NUL)

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from helpers import assert_parity, bits_of, sample_rows, to_device
+from helpers import GROUP_EPS_RANDOM_CODES, assert_parity, bits_of, sample_rows, to_device
 from oracle import bf16_rne_bits, grouped_gemm_bf16, grouped_gemm_f64, plan as oplan, route_ref
 from oracle.gemm import rows_gemm_f64, sa_rows
 
@@ -101,7 +101,7 @@ def _codes_case(lib, counts, N, K, seed, layout=0, exact=False, a_fill=None, sa_
     else:
         mag = grouped_gemm_f64(A, SA_l.reshape(-1), layout, B, SB, off, absolute=True)
         assert_parity(got, ref, f"counts={len(counts)} experts N={N} K={K} layout={layout}", exact=ex64,
-                      abs_sum=mag, K=K)
+                      abs_sum=mag, K=K, group_eps=GROUP_EPS_RANDOM_CODES)
     return got
 
 
@@ -236,7 +236,8 @@ def test_wide_expert_pool(gpu_lib, E, T, skew, N):
         ex64 = grouped_gemm_f64(A, SA_l.reshape(-1), layout, B, SB, off)
         mag = grouped_gemm_f64(A, SA_l.reshape(-1), layout, B, SB, off, absolute=True)
         assert_parity(bits_of(C), bf16_rne_bits(ex64), f"E={E} T={T} skew={skew} N={N} layout={layout} "
-                      f"R={int(off[-1])} max_rows={int(counts.max())}", exact=ex64, abs_sum=mag, K=256)
+                      f"R={int(off[-1])} max_rows={int(counts.max())}", exact=ex64, abs_sum=mag, K=256,
+                      group_eps=GROUP_EPS_RANDOM_CODES)
 
 
 def test_wide_pool_full_size_sampled(gpu_lib):
@@ -272,7 +273,7 @@ def test_wide_pool_full_size_sampled(gpu_lib):
     mag = rows_gemm_f64(*args, cols=cols, absolute=True)
     got = bits_of(C[rows_t][:, torch.from_numpy(cols).cuda()])
     assert_parity(got, bf16_rne_bits(exact), f"wide pool E={E} rows={len(rows)} cols={len(cols)} classes 8+8",
-                  exact=exact, abs_sum=mag, K=K)
+                  exact=exact, abs_sum=mag, K=K, group_eps=GROUP_EPS_RANDOM_CODES)
 
 
 @pytest.mark.parametrize("layout", [0, 1])
@@ -305,4 +306,4 @@ def test_nan_codes_propagate(gpu_lib, layout):
     keep = ~nan_ref.any(axis=1)
     mag = grouped_gemm_f64(A, SA_l.reshape(-1), layout, B, SB, off, absolute=True)
     assert_parity(got[keep], ref[keep], f"rows without NaN, layout={layout}", exact=ex64[keep], abs_sum=mag[keep],
-                  K=384)
+                  K=384, group_eps=GROUP_EPS_RANDOM_CODES)
