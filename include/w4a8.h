@@ -275,6 +275,31 @@ int w4a8_grouped_gemm_planned(const uint8_t* A_fp8_dev, const float* a_scales_de
                               size_t plan_bytes, uint16_t* C_bf16_dev, void* stream);
 
 /*
+ * w4a8_grouped_gemm_planned_noalloc -- w4a8_grouped_gemm_planned for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the plan is built by
+ * w4a8_plan's kernel into the library's own device scratch and the planned
+ * GEMM runs from it, so the caller passes only inputs and outputs.
+ *
+ * max_total_rows     an upper bound on offsets[E] (host value), as for
+ *                    w4a8_plan_bytes.
+ * The scratch is a fixed 4 MiB per device (a plan of up to 262,142 m-tiles),
+ * held from the first call on that device until the process ends; a call
+ * whose w4a8_plan_bytes(E, max_total_rows) exceeds it returns
+ * W4A8_ERR_CAPACITY before any launch.  If the device's offsets[E] exceeds
+ * max_total_rows and the plan then does not fit, its status word says so
+ * and the GEMM writes nothing.  Every call on one device uses the same
+ * scratch, which keeps the last call's plan: calls that overlap on one
+ * device (different streams, or host threads) race and must be ordered by
+ * the caller.  No allocation, no host synchronisation.  Other arguments,
+ * numerics and limits as w4a8_grouped_gemm_planned.
+ */
+int w4a8_grouped_gemm_planned_noalloc(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                                      const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                                      const int32_t* expert_offsets_dev, int E, int N, int K, int64_t max_total_rows,
+                                      uint16_t* C_bf16_dev, void* stream);
+
+/*
  * w4a8_grouped_gemm_swiglu -- the gate/up projection with the step between
  * the two projections fused into its epilogue (humming PR #129 "Results"
  * and PR #58 "H200 performance" time gate/up and down as a pair): the

@@ -14,6 +14,7 @@ torch when the caller does not pass them.
     combine(C, row_of_slot, weights, top_k, out=None) -> per-token bf16 sums
     swiglu_quant(C, layout) -> A (E4M3 codes of silu(gate) * up), SA
     grouped_gemm_planned(A, SA, layout, B, SB, expert_offsets, plan, out=None) -> C (bf16)
+    grouped_gemm_planned_noalloc(A, SA, layout, B, SB, expert_offsets, out) -> out (plan in library scratch)
     grouped_gemm_swiglu(A, SA, layout, B13, SB13, expert_offsets, layout2)
                                      -> A2 (E4M3 codes of silu(gate) * up), SA2
 """
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     combine,
     grouped_gemm,
     grouped_gemm_planned,
+    grouped_gemm_planned_noalloc,
     grouped_gemm_swiglu,
     lib_path,
     load,

@@ -44,6 +44,8 @@ def _declare(lib):
     lib.w4a8_grouped_gemm.restype = i32
     lib.w4a8_grouped_gemm_planned.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp, vp]
     lib.w4a8_grouped_gemm_planned.restype = i32
+    lib.w4a8_grouped_gemm_planned_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.w4a8_grouped_gemm_planned_noalloc.restype = i32
     lib.w4a8_grouped_gemm_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
     lib.w4a8_grouped_gemm_swiglu.restype = i32
     lib.w4a8_swiglu_quant.argtypes = [vp, i32, i32, vp, vp, i32, vp]
@@ -224,6 +226,35 @@ def grouped_gemm_planned(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torc
     _check("w4a8_grouped_gemm_planned", lib.w4a8_grouped_gemm_planned(
         _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K, _ptr(plan),
         plan.numel() * 4, _ptr(out), _stream()))
+    return out
+
+
+def grouped_gemm_planned_noalloc(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor,
+                                 SB: torch.Tensor, expert_offsets: torch.Tensor, out: torch.Tensor,
+                                 max_total_rows: Optional[int] = None) -> torch.Tensor:
+    """The planned GEMM with its plan in the library's device scratch: nothing
+    is allocated, so `out` (bf16 [R, N]) must be given; max_total_rows
+    defaults to R = A.shape[0]."""
+    lib = load()
+    if A.dim() != 2 or B.dim() != 3 or SB.dim() != 3:
+        raise ValueError("A must be [R, K], B [E, N, K/2], SB [E, N, K/32]")
+    R, K = A.shape
+    E, N, Kh = B.shape
+    if Kh * 2 != K or SB.shape != (E, N, K // 32):
+        raise ValueError("inconsistent K between A, B and SB")
+    _need(A, "A", torch.uint8)
+    _need(SA, "a_scales", torch.float32, R * (K // 128))
+    _need(B, "B", torch.uint8)
+    _need(SB, "b_scales", torch.uint8)
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    if out.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("out must be bfloat16 (or 16-bit integer bits)")
+    _need(out, "out", out.dtype, R * N)
+    if R == 0:
+        return out
+    _check("w4a8_grouped_gemm_planned_noalloc", lib.w4a8_grouped_gemm_planned_noalloc(
+        _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
+        int(R if max_total_rows is None else max_total_rows), _ptr(out), _stream()))
     return out
 
 

@@ -29,12 +29,21 @@ int ok() {
   return W4A8_OK;
 }
 
+// Device memory of the allocation-free planned GEMM: the plan of one call
+// (header + 4 int32 per m-tile) lives here instead of in a caller buffer.
+// Each device holds its own copy for the life of the process; host code
+// reaches it only through the address hipGetSymbolAddress gives (kept per
+// device in DeviceInfo::scratch), never through the array's name.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
 struct DeviceInfo {
   bool ready = false;
   bool supported = false;
   int cus = 0;
   int grid = 0;  // workgroups of the persistent GEMM launch (one per CU)
   size_t lds_limit = 0;  // LDS bytes one workgroup may hold
+  int32_t* scratch = nullptr;  // this device's copy of `scratch`
 };
 
 constexpr int kMaxDevices = 64;
@@ -61,6 +70,11 @@ int device_info(const DeviceInfo** out) {
       e = w4a8::grouped_gemm_occupancy(&blocks);
       if (e != hipSuccess) return fail(W4A8_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
       d.grid = d.cus * (blocks > 0 ? blocks : 1);
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || ptr == nullptr)
+        return fail(W4A8_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      d.scratch = static_cast<int32_t*>(ptr);
     }
     d.ready = true;
   }
@@ -217,6 +231,37 @@ int w4a8_grouped_gemm_planned(const uint8_t* A_fp8_dev, const float* a_scales_de
   w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev, C_bf16_dev,
                       E, N, K, a_scale_layout, nullptr, nullptr, 0, 0, (const int32_t*)plan_dev, (int)max_tiles};
   hipError_t e = w4a8::launch_grouped_gemm_planned(args, d->grid, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_planned launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_grouped_gemm_planned_noalloc(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a_scale_layout,
+                                      const uint8_t* B_fp4_dev, const uint8_t* b_scales_e8m0_dev,
+                                      const int32_t* expert_offsets_dev, int E, int N, int K, int64_t max_total_rows,
+                                      uint16_t* C_bf16_dev, void* stream) {
+  int st = check_gemm_shape(E, N, K, W4A8_MAX_PREP_EXPERTS);
+  if (st != W4A8_OK) return st;
+  if (a_scale_layout != W4A8_SCALE_ROW_MAJOR && a_scale_layout != W4A8_SCALE_M_MAJOR)
+    return fail(W4A8_ERR_LAYOUT, "a_scale_layout=%d is neither row-major (0) nor M-major (1)", a_scale_layout);
+  if (!A_fp8_dev || !a_scales_dev || !B_fp4_dev || !b_scales_e8m0_dev || !expert_offsets_dev || !C_bf16_dev)
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(A_fp8_dev, 16) || !aligned(B_fp4_dev, 16) || !aligned(C_bf16_dev, 16) ||
+      !aligned(a_scales_dev, 4) || !aligned(b_scales_e8m0_dev, 4) || !aligned(expert_offsets_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "A, B, C need 16-byte and scales/offsets 4-byte alignment");
+  if (max_total_rows < 0) return fail(W4A8_ERR_SHAPE, "max_total_rows=%lld", (long long)max_total_rows);
+  const size_t need = w4a8_plan_bytes(E, max_total_rows);
+  if (need > kScratchBytes)
+    return fail(W4A8_ERR_CAPACITY, "a plan for E=%d and %lld rows needs %zu bytes; the library's device scratch "
+                "holds %zu", E, (long long)max_total_rows, need, kScratchBytes);
+  const DeviceInfo* d = nullptr;
+  st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  const int max_tiles = (int)((kScratchBytes / sizeof(int32_t) - w4a8::PLAN_HEADER_WORDS) / w4a8::PLAN_TILE_WORDS);
+  hipError_t e = w4a8::launch_plan(expert_offsets_dev, E, N, d->scratch, max_tiles, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  w4a8::GemmArgs args{A_fp8_dev, a_scales_dev, B_fp4_dev, b_scales_e8m0_dev, expert_offsets_dev, C_bf16_dev,
+                      E, N, K, a_scale_layout, nullptr, nullptr, 0, 0, d->scratch, max_tiles};
+  e = w4a8::launch_grouped_gemm_planned(args, d->grid, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_planned launch: %s", hipGetErrorString(e));
   return ok();
 }
