@@ -511,6 +511,79 @@ def measure_gemm_swiglu(reps=10):
 
 
 # ---------------------------------------------------------------------------
+# dense sweep of the tile rule's constants
+# ---------------------------------------------------------------------------
+SWEEP_SHAPES = {"gateup": (4096, 6144), "down": (6144, 2048)}
+SWEEP_TILES = (64, 80, 96, 112, 128)   # MFMA m-tile caps tried (the kernel's largest tile is 128 rows)
+
+
+def sweep_plan(E, rows, cls, tmax, N):
+    """A plan in w4a8_plan's format for E experts of `rows` rows each, every
+    expert in class `cls` (1 streaming, 2 MFMA with m-tiles of at most tmax
+    rows, sized as the tile rule sizes them)."""
+    import torch
+    body = []
+    for e in range(E):
+        r0 = e * rows
+        if cls == 1:
+            body += [e, r0, rows, -(-rows // 16) * 16 | (1 << 16)]
+        else:
+            n = -(-rows // tmax)
+            tm = -(-(-(-rows // n)) // 16) * 16
+            for i in range(n):
+                body += [e, r0 + i * tm, min(tm, rows - i * tm), tm | (2 << 16)]
+    tiles = len(body) // 4
+    ns = tiles if cls == 1 else 0
+    hdr = [0, tiles, ns, tiles - ns, 0, 0, 0, E * rows]
+    return torch.tensor(hdr + body, dtype=torch.int32, device="cuda")
+
+
+def sweep_tiles(rows_list, layouts, reps=10, E=32):
+    """Rows per expert from rows_list (uniform experts, E of them), the two
+    benchmark expert shapes (gate/up N=4096 K=6144, down N=6144 K=2048) and
+    the given scale layouts: the grouped GEMM timed (median of `reps`
+    launches, HIP events) with every expert in the streaming class (rows <=
+    64, the most that class serves) and in the MFMA class with each m-tile
+    cap of SWEEP_TILES, through w4a8_grouped_gemm_planned and plans built
+    here.  Random codes drawn on the GPU; weights rotated past the Infinity
+    Cache.  One JSON line per (shape, layout, rows)."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+
+    for shape, (N, K) in SWEEP_SHAPES.items():
+        Rmax = E * max(rows_list)
+        g = torch.Generator(device="cuda").manual_seed(29)
+        A = torch.randint(0, 256, (Rmax, K), generator=g, dtype=torch.uint8, device="cuda")
+        A[(A & 0x7F) == 0x7F] = 0x38
+        SA0 = torch.rand((Rmax, K // 128), generator=g, device="cuda") * 4 + 0.01
+        wbytes = E * N * K * 17 // 32
+        nrot = _rotations(wbytes)
+        Bs = [torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+              for _ in range(nrot)]
+        SBs = [torch.randint(112, 132, (E, N, K // 32), generator=g, dtype=torch.uint8, device="cuda")
+               for _ in range(nrot)]
+        for layout in layouts:
+            for rows in rows_list:
+                R = E * rows
+                off = torch.arange(0, E + 1, dtype=torch.int32, device="cuda") * rows
+                SA = SA0[:R].contiguous() if layout == 0 else SA0[:R].t().contiguous()
+                C = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+                cands = ([("stream", sweep_plan(E, rows, 1, 0, N))] if rows <= 64 else []) + \
+                        [(f"mfma_t{t}", sweep_plan(E, rows, 2, t, N)) for t in SWEEP_TILES]
+                res = {}
+                for name, plan in cands:
+                    ms = time_launches(lambda i: w4a8.grouped_gemm_planned(
+                        A[:R], SA, layout, Bs[i % nrot], SBs[i % nrot], off, plan, out=C), reps)
+                    res[name] = round(statistics.median(ms) * 1e3, 2)
+                best = min(res, key=res.get)
+                print(json.dumps({"shape": shape, "N": N, "K": K, "E": E, "layout": layout, "rows": rows,
+                                  "us": res, "best": best}), flush=True)
+        del A, SA0, Bs, SBs
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,6 +601,9 @@ def main():
                          "routing-prep and GEMM measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (memory-counter calibration)")
+    ap.add_argument("--sweep-tiles", action="store_true",
+                    help="only run the dense sweep of the tile rule (rows per expert 8..512 step 8, both "
+                         "classes and every MFMA m-tile cap, gate/up and down shapes, both layouts)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -537,6 +613,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.steps or 5)
+        return
+    if args.sweep_tiles:
+        import moe_grouped_precision_amd as w4a8
+        w4a8.load()
+        sweep_tiles(list(range(8, 513, 8)), (0, 1) if args.layout is None else (args.layout,))
         return
 
     import numpy as np
@@ -595,15 +676,12 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / steps
-    # per-launch timing of the grouped GEMM call, on the stream it is launched on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        w.route()
-        ev[i][0].record()
-        w.gemm(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    gemm_ms = [a.elapsed_time(b) for a, b in ev]
+    # per-launch timing of the grouped GEMM call, on the stream it is launched
+    # on, launches queued back to back (the routing prep's offsets do not
+    # change between steps; with a prep before every launch the host's two
+    # calls per step outlast the E=12 launches and the events would time
+    # the host)
+    gemm_ms = time_launches(w.gemm, steps, warmup=0)
     head = w.report(gemm_ms, probes)
     log(f"timed {steps} steps: {ms_per_step * 1e3:.1f} us/step, gemm median {head['gemm_us']['median']} us")
 
