@@ -641,6 +641,8 @@ def main():
         log("measuring sustained peaks (MFMA fp4 x fp8, HBM read)")
         probes = {"mfma_fp4xfp8_tflops": round(probe.mfma_tflops(4, 0), 1),
                   "mfma_fp4xfp8_random_operands_tflops": round(probe.mfma_tflops_random(4, 0), 1),
+                  "mfma_fp4xfp8_zero_acc_tflops": round(probe.mfma_promote_tflops(False), 1),
+                  "mfma_fp4xfp8_zero_acc_promote_tflops": round(probe.mfma_promote_tflops(True), 1),
                   "hbm_read_gbs": round(probe.read_gbs(), 1)}
 
     configs = {}

@@ -40,6 +40,20 @@ int w4a8_probe_mfma_data(int fmt_a, int fmt_b, int iters, int blocks, const int3
                          float* sink_dev, void* stream);
 
 /*
+ * w4a8_probe_mfma_promote -- the grouped GEMM's MFMA-phase instruction
+ * pattern without memory traffic: v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 A,
+ * FP8 B) with a zero accumulator input, eight per iteration, each followed
+ * (promote != 0) by the four fp32 FMAs that scale the partial of the MFMA
+ * two back into an accumulator; promote == 0 issues the MFMAs alone.
+ * `blocks` workgroups of 512 threads (two waves per SIMD), `iters`
+ * iterations per wave, 8 MFMAs of 2*16*16*128 flops each.  ops_dev: int32
+ * [blocks * 512][16] operand words (random bits for a realistic rate);
+ * sink_dev: float [blocks * 512], written.
+ */
+int w4a8_probe_mfma_promote(int promote, int iters, int blocks, const int32_t* ops_dev, float* sink_dev,
+                            void* stream);
+
+/*
  * w4a8_probe_read -- reads `bytes` bytes from buf_dev once (16-byte loads,
  * grid-stride, eight loads in flight per lane) and writes one int to
  * sink_dev.  bytes must be a positive multiple of 16; buf_dev 16-byte aligned.

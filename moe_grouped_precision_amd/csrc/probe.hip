@@ -63,6 +63,54 @@ __global__ void __launch_bounds__(256) mfma_probe_data_kernel(int iters, const i
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The GEMM's MFMA-phase pattern without its memory traffic: 512 threads
+// (two waves per SIMD), operands read per lane from `ops` (random bits), one
+// scale per lane; each iteration issues eight MFMAs with a zero accumulator
+// input (one 128-K group's partial each), and after each one the four fp32
+// FMAs that promote the partial of the MFMA two back into its accumulator
+// with a per-lane scale.  PROMOTE = 0 drops the FMAs (the MFMAs alone).  The
+// operands are made opaque once per iteration so that nothing is hoisted or
+// merged, and every partial is used.
+template <int PROMOTE>
+__global__ void __launch_bounds__(512, 1) mfma_promote_probe_kernel(int iters, const int* __restrict__ ops,
+                                                                    float* sink) {
+  const int* o = ops + ((size_t)blockIdx.x * 512 + threadIdx.x) * 16;
+  v8i a, b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = o[k];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) b[m][k] = o[8 + ((k + m) & 7)];
+  }
+  const float s = 1.0f + (float)(threadIdx.x & 7) * 0.125f;
+  v4f p[8], acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) p[m] = acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+    asm volatile("" : "+v"(a));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) asm volatile("" : "+v"(b[m]));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[m], z, 4, 0, 0, 127, 0, 127);
+      if (PROMOTE) {
+        const int pm = (m + 6) & 7;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[pm][j] = fmaf(s, p[pm][j], acc[pm][j]);
+      } else {
+        asm volatile("" :: "v"(r));
+      }
+      p[m] = r;
+    }
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) t += acc[m][0] + acc[m][1] + acc[m][2] + acc[m][3] + p[m][0];
+  sink[blockIdx.x * 512 + threadIdx.x] = t;
+}
+
 __global__ void __launch_bounds__(256) read_probe_kernel(const v4i* __restrict__ p, size_t n16, int* sink) {
   constexpr int U = 8;
   v4i acc = {0, 0, 0, 0};
@@ -119,5 +167,17 @@ extern "C" int w4a8_probe_mfma_data(int fmt_a, int fmt_b, int iters, int blocks,
     hipLaunchKernelGGL((mfma_probe_data_kernel<4, 4>), dim3(blocks), dim3(256), 0, s, iters, ops_dev, sink_dev);
   else
     return W4A8_ERR_SHAPE;
+  return hipGetLastError() == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+extern "C" int w4a8_probe_mfma_promote(int promote, int iters, int blocks, const int32_t* ops_dev, float* sink_dev,
+                                       void* stream) {
+  if (!sink_dev || !ops_dev) return W4A8_ERR_NULL;
+  if (iters <= 0 || blocks <= 0) return W4A8_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (promote)
+    hipLaunchKernelGGL((mfma_promote_probe_kernel<1>), dim3(blocks), dim3(512), 0, s, iters, ops_dev, sink_dev);
+  else
+    hipLaunchKernelGGL((mfma_promote_probe_kernel<0>), dim3(blocks), dim3(512), 0, s, iters, ops_dev, sink_dev);
   return hipGetLastError() == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }

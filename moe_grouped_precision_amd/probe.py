@@ -27,6 +27,9 @@ def load():
         lib.w4a8_probe_mfma_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.w4a8_probe_mfma_data.restype = ctypes.c_int
+        lib.w4a8_probe_mfma_promote.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        lib.w4a8_probe_mfma_promote.restype = ctypes.c_int
         lib.w4a8_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p]
         lib.w4a8_probe_read.restype = ctypes.c_int
@@ -88,6 +91,29 @@ def mfma_tflops_random(fmt_a: int, fmt_b: int, iters: int = 4096, reps: int = 5,
 
     ms = _time(run, reps)
     flops = blocks * 4 * iters * 8 * MFMA_FLOPS
+    return flops / (ms * 1e-3) / 1e12
+
+
+def mfma_promote_tflops(promote: bool, iters: int = 4096, reps: int = 5, seed: int = 0) -> float:
+    """Sustained TFLOP/s (MFMA flops only) of the GEMM's MFMA-phase pattern
+    without memory traffic: FP4 x FP8 MFMAs with a zero accumulator input on
+    random operands, each followed (promote) by four fp32 promotion FMAs;
+    one 512-thread workgroup per CU (two waves per SIMD, as the GEMM)."""
+    lib = load()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    ops = torch.randint(-2**31, 2**31 - 1, (blocks * 512 * 16,), dtype=torch.int32, device="cuda", generator=g)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        st = lib.w4a8_probe_mfma_promote(int(promote), iters, blocks, ctypes.c_void_p(ops.data_ptr()),
+                                         ctypes.c_void_p(sink.data_ptr()), stream)
+        if st != 0:
+            raise RuntimeError(f"w4a8_probe_mfma_promote status {st}")
+
+    ms = _time(run, reps)
+    flops = blocks * 8 * iters * 8 * MFMA_FLOPS
     return flops / (ms * 1e-3) / 1e12
 
 

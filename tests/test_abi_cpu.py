@@ -219,7 +219,7 @@ def test_probe_library_exports_and_host_checks():
     if not os.path.exists(path):
         pytest.skip("probe library not built")
     probe = ctypes.CDLL(path)
-    for name in ("w4a8_probe_mfma", "w4a8_probe_mfma_data", "w4a8_probe_read"):
+    for name in ("w4a8_probe_mfma", "w4a8_probe_mfma_data", "w4a8_probe_mfma_promote", "w4a8_probe_read"):
         assert hasattr(probe, name)
     probe.w4a8_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
