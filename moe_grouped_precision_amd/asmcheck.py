@@ -14,7 +14,11 @@ kernel, two properties the compiler can no longer guarantee by itself:
   is at least 5 wait states after the last VALU write of that SGPR.
 
 The dataflow is conservative: at a merge point a register is pending if it
-may be pending on any incoming path.  Exit status 1 lists each finding.
+may be pending on any incoming path.  Long branches (s_getpc_b64 / add /
+s_setpc_b64, which the compiler emits when a kernel outgrows the short branch
+range) are followed to their targets, and a kernel with any block the parsed
+control-flow graph does not reach is itself a finding, so the check cannot
+silently skip code.  Exit status 1 lists each finding.
 """
 
 from __future__ import annotations
@@ -80,6 +84,9 @@ def _parse(lines):
     return kernels
 
 
+_LONG_TARGET = re.compile(r"\((\.L\w+)-\.Lpost_getpc\w*\)")
+
+
 def _successors(kern, bi):
     blk = kern["blocks"][bi]
     succ = []
@@ -88,6 +95,16 @@ def _successors(kern, bi):
     m = _BRANCH.match(last)
     if m and m.group(2) in kern["labels"]:
         succ.append(kern["labels"][m.group(2)])
+    if op.startswith("s_setpc"):
+        # a long branch: s_getpc_b64, then the target's distance added to the
+        # pc in the same block, then s_setpc_b64 -- its target is a successor
+        for _, text in blk["ins"]:
+            t = _LONG_TARGET.search(text)
+            if t and t.group(1) in kern["labels"]:
+                succ.append(kern["labels"][t.group(1)])
+                break
+        else:
+            raise ValueError(f"s_setpc_b64 with no recognisable target in block {blk['label']}")
     if op not in ("s_branch", "s_endpgm") and not op.startswith("s_setpc"):
         if bi + 1 < len(kern["blocks"]):
             succ.append(bi + 1)
@@ -185,10 +202,30 @@ def _check_kernel(kern, findings):
                 work.append(s)
 
 
+def _unreached(kern):
+    """Blocks with instructions that the CFG does not reach from the entry
+    (the check would say nothing about them)."""
+    seen, stack = {0}, [0]
+    while stack:
+        b = stack.pop()
+        for s in _successors(kern, b):
+            if s not in seen:
+                seen.add(s)
+                stack.append(s)
+    return [b for b in range(len(kern["blocks"])) if b not in seen and kern["blocks"][b]["ins"]]
+
+
 def check(path: str):
     lines = open(path).read().split("\n")
     findings = []
     for kern in _parse(lines):
+        if kern["name"].startswith(("amdhsa.", "__hip_cuid")):
+            continue   # metadata sections after the kernels
+        un = _unreached(kern)
+        if un:
+            b = kern["blocks"][un[0]]
+            findings.append(f"{kern['name']}: {len(un)} block(s) unreachable in the parsed CFG, first at line "
+                            f"{b['ins'][0][0]} -- the check would not cover them")
         _check_kernel(kern, findings)
     return findings
 

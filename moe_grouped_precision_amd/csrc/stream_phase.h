@@ -483,4 +483,434 @@ __device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Continuous streaming: all of a workgroup's streaming items as one pipeline.
+//
+// The per-item schedule above fills its two-stage pipeline at the start of
+// every item and drains it at the end.  Here a workgroup runs a sequence of
+// items of one row-block count MB (the same register ring shape) back to
+// back: the last two stages of an item issue the loads of the next item's
+// first two stages, so the next item starts with its data on the way.
+//   * stage S-2 of an item issues the next item's stage 0 (activation rows
+//     into ring slot (t+2) % 3, weights into the register slot it frees);
+//   * stage S-1 issues loads with exec = 0 (they count, read nothing);
+//   * after its last stage the item's K halves are added through two free
+//     ring slots (t % 3, which stage t has finished reading, and
+//     (t+2) % 3), the bf16 results stored, and only then are the next
+//     item's scale chunk 0 and stage 1 issued (into slot (t+2) % 3 and the
+//     register slot stage t freed).  Issuing them after the stores keeps
+//     every wait one constant: the loads newer than a stage's weights are
+//     always exactly one stage's worth (the stores, older, only make the
+//     first wait of the next item also wait for them).
+// Scale chunks alternate between two buffers by a chunk count kept across
+// items; a chunk is loaded two stages before its first one, or for chunk 0
+// of a following item after the reduction, when every chunk of the item
+// before is done.  Items need at least two stages (K >= 640); an odd stage
+// count is run as the next even one (see run()).  Numerics are
+// those of the per-item schedule (the same groups in the same order, the
+// halves added half 0 + half 1), so results do not depend on which
+// schedule ran.
+// ---------------------------------------------------------------------------
+struct StreamWork {  // expert e, rows [row0, row0 + rows), columns n0 .. n0 + 64 w - 1
+  int e, row0, rows, n0, w;
+  bool valid;
+};
+
+template <int NBW, int MB>
+struct StreamRun {
+  static constexpr int KG = P1_KG, D = 2, NX = 3;
+  static constexpr int XSLOT = KG * P1_XGROUP;
+  static constexpr int PER = KG * (NBW + MB);   // loads per wave per stage
+  static constexpr int WIDTH = 64 * NBW;
+  static constexpr int SBS = stream_sb_stride(NBW);
+  static constexpr int SAB = P1_SB + 2 * SBS;
+  static constexpr int MBA = (MB + 1) / 2;       // row blocks reduced through the first free slot
+  static_assert(KG == 2 && D == 2, "written for two groups per stage and two stages in flight");
+  static_assert(NX * XSLOT <= P1_XRING, "activation ring");
+  static_assert(NBW * MBA * 4 * 1024 <= XSLOT, "a reduction region fits one ring slot");
+  static_assert(SBS >= 2 * 64 * NBW * SC * 4 && SAB + 2 * P1_SABUF <= P1_BYTES, "scale chunk buffers");
+  static_assert((D - 1) * PER < 64, "vmcnt range");
+  static_assert(NBW <= stream_max_nbw(MB), "register budget");
+
+  const GemmArgs& p;
+  uint8_t* lds;
+  int R, G, Gh, S, kh, wn, gbase, gcount;
+
+  __device__ __forceinline__ StreamRun(const GemmArgs& p_, uint8_t* lds_, int R_) : p(p_), lds(lds_), R(R_) {
+    const int wave = threadIdx.x >> 6;
+    G = p.K >> 7;
+    Gh = (G + 1) / 2;
+    S = (Gh + KG - 1) / KG;
+    kh = uniform(wave >> 2);
+    wn = uniform(wave & 3);
+    gbase = kh ? Gh : 0;
+    gcount = kh == 0 ? Gh : G - Gh;
+  }
+
+  // Activation rows of item stage s into ring slot `slot`: 2 groups x 2 halves
+  // x 64 rows x 128 B, MB loads of 4 rows per wave and group.
+  __device__ __forceinline__ void issue_x(const StreamWork& it, int s, int slot, bool live) const {
+    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
+    const int K = p.K;
+    const uint8_t* xt = p.A + (size_t)it.row0 * K;
+    const uint64_t mask = live_mask(live) & 0xffffffffull;  // lanes 0-31 load
+    const int sc = min(s, S - 1);
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const int g0 = min(sc * KG + kg, G - 1), g1 = min(Gh + sc * KG + kg, G - 1);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int jx = wave * MB + i;
+        const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
+        const int r = quad * 4 + (lane >> 3);
+        const uint32_t xo = (uint32_t)min(r, it.rows - 1) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 4);
+        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo,
+                 lds_u32(lds + slot * XSLOT + kg * P1_XGROUP + h * 8192 + quad * 512), mask);
+      }
+    }
+  }
+
+  // Weights of item stage s for this wave (the layout of StreamItem::load_w):
+  // blocks outside the item's width load nothing.
+  __device__ __forceinline__ void issue_w(const StreamWork& it, int s, v4i (&w)[KG][NBW], bool live) const {
+    const int lane = opaque_lane();
+    const int q = lane >> 4, r16 = lane & 15;
+    const int K = p.K, N = p.N;
+    const uint8_t* wt = p.B + ((size_t)it.e * N + it.n0) * (size_t)(K >> 1);
+    const uint32_t goff = (uint32_t)min(gbase + min(s, S - 1) * KG + (r16 >> 3), G - 1) * 64u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int b16 = uniform((wn * NBW + j) * 16);
+        const int n = min(it.n0 + b16 + 8 * h + (r16 & 7), N - 1);
+        const uint32_t wo = (uint32_t)(n - it.n0) * (uint32_t)(K >> 1) + q * 16;
+        vm_load16_nt(w[h][j], wt, wo + goff, live_mask(live && b16 < 64 * it.w));
+      }
+  }
+
+  // Scale chunk c of an item (groups SC c .. SC c + 3 of each half) into buffer buf.
+  __device__ __forceinline__ void issue_scales(const StreamWork& it, int c, int buf) const {
+    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
+    const int K = p.K, N = p.N;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const int idx = (wave * NBW + i) * 64 + lane;  // [h][col][gg]
+      const int h = idx / (WIDTH * SC), rem = idx - h * (WIDTH * SC);
+      const int col = rem >> 2, gg = rem & 3;
+      const int n = min(it.n0 + col, N - 1);
+      const int g = min((h ? Gh : 0) + SC * c + gg, G - 1);
+      vm_dma4(p.SB + ((size_t)it.e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+              lds_u32(lds + P1_SB + buf * SBS + (wave * NBW + i) * 256));
+    }
+    const int idx = wave * 64 + lane;  // [h][row][gg]
+    const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
+    const size_t row = (size_t)it.row0 + min(r, it.rows - 1);
+    const int g = min((h ? Gh : 0) + SC * c + gg, G - 1);
+    vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + SAB + buf * P1_SABUF + wave * 256));
+  }
+
+  // The MFMAs and promotions of item stage s.
+  __device__ __forceinline__ void compute(int s, int xslot, int sbuf, const v4i (&w)[KG][NBW],
+                                          v4f (&acc)[NBW][MB]) const {
+    const int lane = opaque_lane();
+    const int q = lane >> 4, r16 = lane & 15;
+    const uint8_t* slot = lds + xslot * XSLOT;
+    const uint8_t* sbb = lds + P1_SB + sbuf * SBS;
+    const uint8_t* sab = lds + SAB + sbuf * P1_SABUF;
+    v4i wop[KG][NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) StreamItem<NBW, KG, MB>::pair_operands(w[0][j], w[1][j], wop[0][j], wop[1][j]);
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const int gl = s * KG + kg;  // group index within this wave's half
+      if (gl < gcount) {
+        const int gg = gl % SC;
+        int sbv[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const int col = (wn * NBW + j) * 16 + r16;
+          sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int m = i * 16 + r16;
+          const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
+          const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
+          const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
+          const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) promote(acc[j][i], sa, mfma_group(wop[kg][j], x0, x1, sbv[j]));
+        }
+      }
+    }
+  }
+
+  // Wait for the weights of the stage about to run (exactly one later stage's
+  // loads may be in flight), make them readable, meet the other waves.
+  __device__ __forceinline__ static void stage_wait(v4i (&w)[KG][NBW]) {
+    wait_vm<(D - 1) * PER>();
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) tie(w[kg][j]);
+    wg_barrier();
+  }
+
+  // Add the K halves of an item through ring slots ra and rb (row blocks
+  // below MBA in ra, the rest in rb) and store the bf16 result.
+  __device__ __forceinline__ void reduce_store(const StreamWork& it, int ra, int rb, v4f (&acc)[NBW][MB]) const {
+    const int lane = opaque_lane();
+    const int q = lane >> 4, r16 = lane & 15;
+    __syncthreads();  // every wave is past its last LDS read of the item
+    v4f* red_a = reinterpret_cast<v4f*>(lds + ra * XSLOT) + uniform(wn) * 64 + lane;
+    v4f* red_b = reinterpret_cast<v4f*>(lds + rb * XSLOT) + uniform(wn) * 64 + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          if (i < MBA) red_a[(j * MBA + i) * 256] = acc[j][i];
+          else red_b[(j * MBA + i - MBA) * 256] = acc[j][i];
+        }
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const int N = p.N;
+      const int nend = min(N, it.n0 + 64 * it.w);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = i * 16 + r16;
+        if (m < it.rows) {
+          uint16_t* crow = p.C + (size_t)(it.row0 + m) * N;
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int n = it.n0 + (wn * NBW + j) * 16 + q * 4;
+            const v4f o = i < MBA ? red_a[(j * MBA + i) * 256] : red_b[(j * MBA + i - MBA) * 256];
+            if (n < nend) store_bf16x4(crow + n, acc[j][i] + o);
+          }
+        }
+      }
+    }
+    __syncthreads();  // the two regions are reloaded next
+  }
+
+  template <class Source>
+  __device__ __forceinline__ void run(Source& src) {
+    StreamWork cur = src.next();
+    if (!cur.valid) return;
+    StreamWork nxt = src.next();
+    v4i wr[D][KG][NBW];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) wr[u][kg][j] = v4i{0, 0, 0, 0};
+    const int SE = S + (S & 1);  // stages run per item (even)
+    const int C = SE / 2;        // scale chunks per item (two stages each)
+    // prologue of the first item: scale chunk 0, stages 0 and 1
+    issue_scales(cur, 0, 0);
+    issue_x(cur, 0, 0, true);
+    issue_w(cur, 0, wr[0], true);
+    issue_x(cur, 1, 1, true);
+    issue_w(cur, 1, wr[1], true);
+    int t = 0;      // global stage of the workgroup's pipeline
+    int base = 0;   // global chunk number of the item's chunk 0
+    for (;;) {
+      v4f acc[NBW][MB];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+      // a stand-in with valid addresses for the loads of a missing next item
+      const StreamWork nx = nxt.valid ? nxt : cur;
+      // item stage s uses register slot s & 1: items run an even number of
+      // stages (an odd count gets one more, without MFMAs, whose loads are
+      // issued with exec = 0), so every item starts on slot 0 and the loop
+      // has one body -- the ring registers keep their places and are never
+      // copied while their loads are in flight
+      auto stage = [&](int s, int u) __attribute__((always_inline)) {
+        stage_wait(wr[u]);
+        // the loads this stage issues, for stage sn = s + 2: the item's own
+        // stage, the next item's stage 0 (sn == SE), or none (exec = 0: the
+        // padding stage, the last stage, a missing next item).  One load
+        // site per ring register, with no branch around it, so that the
+        // register is one value the compiler never copies.
+        const int sn = s + 2;
+        const bool own = sn < S, next0 = sn == SE;
+        const StreamWork wi = own ? cur : nx;
+        const int ws = own ? sn : 0;
+        const bool live = own || (next0 && nxt.valid);
+        if (own && (sn & 1) == 0) issue_scales(cur, sn >> 1, (base + (sn >> 1)) & 1);
+        issue_x(wi, ws, (t + 2) % NX, live);
+        if (s < S) compute(s, t % NX, (base + (s >> 1)) & 1, wr[u], acc);
+        issue_w(wi, ws, wr[u], live);
+        ++t;
+      };
+      for (int s = 0; s < SE; s += 2) {
+        stage(s, 0);
+        stage(s + 1, 1);
+      }
+      // t is now one past the item's last stage: its slot (t - 1) % 3 and
+      // slot (t + 1) % 3 are free; slot t % 3 holds the next item's stage 0
+      reduce_store(cur, (t + 2) % NX, (t + 1) % NX, acc);
+      if (!nxt.valid) break;
+      // the next item's scale chunk 0 and stage 1, after the stores
+      const int nbase = base + C;
+      issue_scales(nxt, 0, nbase & 1);
+      issue_x(nxt, 1, (t + 1) % NX, true);
+      issue_w(nxt, 1, wr[1], true);
+      base = nbase;
+      cur = nxt;
+      nxt = src.next();
+    }
+    // every load has retired; the ties keep the ring registers reserved until here
+    wait_vm<0>();
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) tie(wr[u][kg][j]);
+  }
+};
+
+// Work split for the continuous pipeline.  The streaming experts are grouped
+// by row blocks (MB = 1..4, one register ring shape each); every class gets
+// a share of the workgroups proportional to its cost, units x (6 + MB) (a
+// 64-column unit streams 6 KB of weights per stage against MB KB of
+// activation rows), with at least one workgroup for a class that has tiles;
+// inside a class, workgroup b' of G_c streams the contiguous units
+// [U_c b' / G_c, U_c (b' + 1) / G_c) of the class's U_c = tiles x units
+// (a range may cross from one expert to the next; an item never does).
+//   s_eord[k]    expert at class-ordered position k
+//   s_cls[c]     class c: {tiles, first position, first workgroup, workgroups}
+// Wave 0 fills them; every thread must call it.
+__device__ __forceinline__ void stream_class_plan(const int* s_off, int E, int nu, int grid, int* s_eord,
+                                                  int (*s_cls)[4]) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (E + 63) / 64;
+    const int i0 = lane * per;
+    int cnt[4] = {0, 0, 0, 0};
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int c = (rows - 1) >> 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cnt[j] += j == c;
+        }
+      }
+    }
+    int pre[4], tot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int incl = wave_inclusive_sum(cnt[j]);
+      pre[j] = incl - cnt[j];
+      tot[j] = __builtin_amdgcn_readlane(incl, 63);
+    }
+    int pos0[4], nonempty = 0;
+    double cost[4], total = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pos0[j] = j == 0 ? 0 : pos0[j - 1] + tot[j - 1];
+      cost[j] = (double)tot[j] * nu * (6 + j + 1);
+      total += cost[j];
+      nonempty += tot[j] > 0;
+    }
+    // one workgroup per nonempty class, the rest by cumulative cost
+    const int rest = grid - nonempty;
+    int g0[4], gn[4];
+    double cum = 0.0;
+    int given = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lo = (int)((double)rest * cum / total);
+      cum += cost[j];
+      const int hi = j == 3 ? rest : (int)((double)rest * cum / total);
+      g0[j] = given + lo;
+      gn[j] = tot[j] > 0 ? 1 + hi - lo : 0;
+      given += tot[j] > 0 ? 1 : 0;
+    }
+    int next[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) next[j] = pos0[j] + pre[j];
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int c = (rows - 1) >> 4;
+          int pos = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j == c) pos = next[j]++;
+          s_eord[pos] = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane == j) {
+        s_cls[j][0] = tot[j];
+        s_cls[j][1] = pos0[j];
+        s_cls[j][2] = g0[j];
+        s_cls[j][3] = gn[j];
+      }
+  }
+  __syncthreads();
+}
+
+// The items of one workgroup's range of a class: [u, u_end) over the class's
+// tiles (class-ordered experts from pos0), at most W units per item and
+// never across an expert boundary.
+struct StreamRangeSource {
+  const int* s_off;
+  const int* s_eord;
+  int pos0, nu, W;
+  long long u, u_end;
+  __device__ __forceinline__ StreamWork next() {
+    StreamWork it{0, 0, 0, 0, 0, false};
+    if (u >= u_end) return it;
+    const int k = (int)(u / nu);
+    const int c0 = (int)(u - (long long)k * nu);
+    it.w = (int)min((long long)min(W, nu - c0), u_end - u);
+    it.e = uniform(s_eord[pos0 + k]);
+    it.row0 = uniform(s_off[it.e]);
+    it.rows = uniform(s_off[it.e + 1]) - it.row0;
+    it.n0 = c0 * 64;
+    it.valid = true;
+    u += it.w;
+    return it;
+  }
+};
+
+// Streaming phase of one workgroup with the continuous pipeline (K >= 640).
+__device__ __forceinline__ void stream_phase_continuous(const GemmArgs& p, uint8_t* lds, const int* s_off,
+                                                        int* s_eord, int (*s_cls)[4], int R) {
+  const int nu = (p.N + 63) / 64;
+  stream_class_plan(s_off, p.E, nu, gridDim.x, s_eord, s_cls);
+  const int b = blockIdx.x;
+  int c = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int g0 = uniform(s_cls[j][2]), gn = uniform(s_cls[j][3]);
+    if (b >= g0 && b < g0 + gn) c = j;
+  }
+  if (c < 0) return;
+  const int tiles = uniform(s_cls[c][0]), gn = uniform(s_cls[c][3]), bl = b - uniform(s_cls[c][2]);
+  const long long U = (long long)tiles * nu;
+  StreamRangeSource src{s_off, s_eord, uniform(s_cls[c][1]), nu, P1_RANGE_MAXNBW, U * bl / gn, U * (bl + 1) / gn};
+  switch (c) {
+    case 0: StreamRun<P1_RANGE_MAXNBW, 1>(p, lds, R).run(src); break;
+    case 1: StreamRun<P1_RANGE_MAXNBW, 2>(p, lds, R).run(src); break;
+    case 2: StreamRun<P1_RANGE_MAXNBW, 3>(p, lds, R).run(src); break;
+    default: StreamRun<P1_RANGE_MAXNBW, 4>(p, lds, R).run(src); break;
+  }
+}
+
 }  // namespace w4a8

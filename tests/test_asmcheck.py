@@ -99,3 +99,33 @@ def test_pending_load_across_a_branch_merge(tmp_path):
         s_waitcnt vmcnt(0)
     """)
     assert any("reads VGPR v5" in x for x in f)
+
+
+def test_long_branch_target_is_followed(tmp_path):
+    # a kernel too large for short branches jumps through s_getpc/s_setpc; the
+    # target's code must be checked with the state the branch carries
+    f = _check(tmp_path, """
+        global_load_dwordx4 v[0:3], v10, s[2:3]
+        s_getpc_b64 s[8:9]
+    .Lpost_getpc0:
+        s_add_u32 s8, s8, (.LBB0_2-.Lpost_getpc0)&4294967295
+        s_addc_u32 s9, s9, (.LBB0_2-.Lpost_getpc0)>>32
+        s_setpc_b64 s[8:9]
+    .LBB0_1:
+        s_nop 0
+    .LBB0_2:
+        v_mov_b64_e32 v[20:21], v[0:1]
+    """)
+    assert any("reads VGPR v0" in x for x in f)
+
+
+def test_unreachable_code_is_reported(tmp_path):
+    # code the parsed control-flow graph cannot reach would escape the check
+    f = _check(tmp_path, """
+        s_branch .LBB0_2
+    .LBB0_1:
+        v_mov_b32_e32 v1, v2
+    .LBB0_2:
+        s_nop 0
+    """)
+    assert any("unreachable" in x for x in f)
