@@ -490,32 +490,42 @@ __device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid,
 // The per-item schedule above fills its two-stage pipeline at the start of
 // every item and drains it at the end.  Here a workgroup runs a sequence of
 // items of one row-block count MB (the same register ring shape) back to
-// back: the last two stages of an item issue the loads of the next item's
-// first two stages, so the next item starts with its data on the way.
-//   * stage S-2 of an item issues the next item's stage 0 (activation rows
-//     into ring slot (t+2) % 3, weights into the register slot it frees);
-//   * stage S-1 issues loads with exec = 0 (they count, read nothing);
-//   * after its last stage the item's K halves are added through two free
-//     ring slots (t % 3, which stage t has finished reading, and
-//     (t+2) % 3), the bf16 results stored, and only then are the next
-//     item's scale chunk 0 and stage 1 issued (into slot (t+2) % 3 and the
-//     register slot stage t freed).  Issuing them after the stores keeps
-//     every wait one constant: the loads newer than a stage's weights are
-//     always exactly one stage's worth (the stores, older, only make the
-//     first wait of the next item also wait for them).
+// back, and the pipeline does not stop between them: stage s of an item
+// issues the loads of stage s + 2, and past the item's end those are the
+// next item's stages 0 and 1 (its scale chunk 0 with stage 0).  So when an
+// item's last stage has run, the next item's first two stages are already
+// on the way, and only the addition of the item's K halves (through the one
+// activation-ring slot no load is filling: the last stage's) separates the
+// two.  Items run an even number of stages (an odd count gets one more,
+// without MFMAs, whose loads are issued with exec = 0), so stage s always
+// uses register slot s & 1 and the loop has one body: the ring registers
+// keep their places and are never copied while their loads are in flight.
+// Every stage issues exactly one stage's worth of loads from one branch-free
+// site per register (exec = 0 where there is nothing to load), so every
+// wait is the same constant; the bf16 stores of a reduction, issued after
+// the next item's loads, only make the next two waits also wait for them.
 // Scale chunks alternate between two buffers by a chunk count kept across
-// items; a chunk is loaded two stages before its first one, or for chunk 0
-// of a following item after the reduction, when every chunk of the item
-// before is done.  Items need at least two stages (K >= 640); an odd stage
-// count is run as the next even one (see run()).  Numerics are
-// those of the per-item schedule (the same groups in the same order, the
-// halves added half 0 + half 1), so results do not depend on which
-// schedule ran.
+// items.  Items need at least two stages (K >= 640).  Numerics are those
+// of the per-item schedule (the same groups in the same order, the halves
+// added half 0 + half 1), so results do not depend on which schedule ran.
 // ---------------------------------------------------------------------------
 struct StreamWork {  // expert e, rows [row0, row0 + rows), columns n0 .. n0 + 64 w - 1
   int e, row0, rows, n0, w;
   bool valid;
 };
+
+// c ? a : b field by field (a whole-struct select makes the compiler pick
+// between the two objects' addresses, i.e. keep them in memory).
+__device__ __forceinline__ StreamWork pick(bool c, const StreamWork& a, const StreamWork& b) {
+  StreamWork r;
+  r.e = c ? a.e : b.e;
+  r.row0 = c ? a.row0 : b.row0;
+  r.rows = c ? a.rows : b.rows;
+  r.n0 = c ? a.n0 : b.n0;
+  r.w = c ? a.w : b.w;
+  r.valid = c ? a.valid : b.valid;
+  return r;
+}
 
 template <int NBW, int MB>
 struct StreamRun {
@@ -525,10 +535,11 @@ struct StreamRun {
   static constexpr int WIDTH = 64 * NBW;
   static constexpr int SBS = stream_sb_stride(NBW);
   static constexpr int SAB = P1_SB + 2 * SBS;
-  static constexpr int MBA = (MB + 1) / 2;       // row blocks reduced through the first free slot
+  // row blocks added per pass of the reduction through one ring slot
+  static constexpr int MBP = (8 / NBW) < MB ? (8 / NBW) : MB;
   static_assert(KG == 2 && D == 2, "written for two groups per stage and two stages in flight");
   static_assert(NX * XSLOT <= P1_XRING, "activation ring");
-  static_assert(NBW * MBA * 4 * 1024 <= XSLOT, "a reduction region fits one ring slot");
+  static_assert(NBW * MBP * 4 * 1024 <= XSLOT && MBP >= 1, "a reduction pass fits one ring slot");
   static_assert(SBS >= 2 * 64 * NBW * SC * 4 && SAB + 2 * P1_SABUF <= P1_BYTES, "scale chunk buffers");
   static_assert((D - 1) * PER < 64, "vmcnt range");
   static_assert(NBW <= stream_max_nbw(MB), "register budget");
@@ -548,45 +559,62 @@ struct StreamRun {
     gcount = kh == 0 ? Gh : G - Gh;
   }
 
-  // Activation rows of item stage s into ring slot `slot`: 2 groups x 2 halves
-  // x 64 rows x 128 B, MB loads of 4 rows per wave and group.
-  __device__ __forceinline__ void issue_x(const StreamWork& it, int s, int slot, bool live) const {
+  // This lane's offsets of an item: activation rows (row clamped to the
+  // item's rows, 16-byte chunk swizzled) and weight columns (clamped to N).
+  __device__ __forceinline__ void offsets(const StreamWork& it, uint32_t (&xo)[MB], uint32_t (&wo)[2][NBW]) const {
     const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
-    const int K = p.K;
-    const uint8_t* xt = p.A + (size_t)it.row0 * K;
-    const uint64_t mask = live_mask(live) & 0xffffffffull;  // lanes 0-31 load
-    const int sc = min(s, S - 1);
+    const int q = lane >> 4, r16 = lane & 15;
+    const int K = p.K, N = p.N;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int jx = wave * MB + i;
+      const int quad = jx % (4 * MB);
+      const int r = quad * 4 + (lane >> 3);
+      xo[i] = (uint32_t)min(r, it.rows - 1) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 4);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int n = min(it.n0 + (wn * NBW + j) * 16 + 8 * h + (r16 & 7), N - 1);
+        wo[h][j] = (uint32_t)(n - it.n0) * (uint32_t)(K >> 1) + q * 16;
+      }
+  }
+
+  // Activation rows of item stage s into ring slot `slot` (2 groups x 2
+  // halves x 64 rows x 128 B; MB loads of 4 rows per wave and group, lanes
+  // 0-31 load).
+  __device__ __forceinline__ void issue_x(const StreamWork& it, const uint32_t (&xo)[MB], int s, int slot,
+                                          bool live) const {
+    const int wave = uniform(threadIdx.x >> 6);
+    const uint8_t* xt = p.A + (size_t)it.row0 * p.K;
+    const uint64_t mask = live_mask(live) & 0xffffffffull;
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
-      const int g0 = min(sc * KG + kg, G - 1), g1 = min(Gh + sc * KG + kg, G - 1);
+      const int g0 = min(s * KG + kg, G - 1), g1 = min(Gh + s * KG + kg, G - 1);
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int jx = wave * MB + i;
         const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
-        const int r = quad * 4 + (lane >> 3);
-        const uint32_t xo = (uint32_t)min(r, it.rows - 1) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 4);
-        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo,
+        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
                  lds_u32(lds + slot * XSLOT + kg * P1_XGROUP + h * 8192 + quad * 512), mask);
       }
     }
   }
 
-  // Weights of item stage s for this wave (the layout of StreamItem::load_w):
+  // Weights of item stage s for this wave (the layout of StreamItem::load_w);
   // blocks outside the item's width load nothing.
-  __device__ __forceinline__ void issue_w(const StreamWork& it, int s, v4i (&w)[KG][NBW], bool live) const {
-    const int lane = opaque_lane();
-    const int q = lane >> 4, r16 = lane & 15;
-    const int K = p.K, N = p.N;
-    const uint8_t* wt = p.B + ((size_t)it.e * N + it.n0) * (size_t)(K >> 1);
-    const uint32_t goff = (uint32_t)min(gbase + min(s, S - 1) * KG + (r16 >> 3), G - 1) * 64u;
+  __device__ __forceinline__ void issue_w(const StreamWork& it, const uint32_t (&wo)[2][NBW], int s,
+                                          v4i (&w)[KG][NBW], bool live) const {
+    const int r16 = opaque_lane() & 15;
+    const uint8_t* wt = p.B + ((size_t)it.e * p.N + it.n0) * (size_t)(p.K >> 1);
+    const uint32_t goff = (uint32_t)min(gbase + s * KG + (r16 >> 3), G - 1) * 64u;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const int b16 = uniform((wn * NBW + j) * 16);
-        const int n = min(it.n0 + b16 + 8 * h + (r16 & 7), N - 1);
-        const uint32_t wo = (uint32_t)(n - it.n0) * (uint32_t)(K >> 1) + q * 16;
-        vm_load16_nt(w[h][j], wt, wo + goff, live_mask(live && b16 < 64 * it.w));
+        vm_load16_nt(w[h][j], wt, wo[h][j] + goff, live_mask(live && b16 < 64 * it.w));
       }
   }
 
@@ -648,7 +676,8 @@ struct StreamRun {
   }
 
   // Wait for the weights of the stage about to run (exactly one later stage's
-  // loads may be in flight), make them readable, meet the other waves.
+  // loads may be in flight, or stores older than them), make them readable,
+  // meet the other waves.
   __device__ __forceinline__ static void stage_wait(v4i (&w)[KG][NBW]) {
     wait_vm<(D - 1) * PER>();
 #pragma unroll
@@ -658,42 +687,40 @@ struct StreamRun {
     wg_barrier();
   }
 
-  // Add the K halves of an item through ring slots ra and rb (row blocks
-  // below MBA in ra, the rest in rb) and store the bf16 result.
-  __device__ __forceinline__ void reduce_store(const StreamWork& it, int ra, int rb, v4f (&acc)[NBW][MB]) const {
+  // Add the K halves of an item through ring slot rs, MBP row blocks per
+  // pass, and store the bf16 result.
+  __device__ __forceinline__ void reduce_store(const StreamWork& it, int rs, v4f (&acc)[NBW][MB]) const {
     const int lane = opaque_lane();
     const int q = lane >> 4, r16 = lane & 15;
-    __syncthreads();  // every wave is past its last LDS read of the item
-    v4f* red_a = reinterpret_cast<v4f*>(lds + ra * XSLOT) + uniform(wn) * 64 + lane;
-    v4f* red_b = reinterpret_cast<v4f*>(lds + rb * XSLOT) + uniform(wn) * 64 + lane;
-    if (kh == 1) {
+    v4f* red = reinterpret_cast<v4f*>(lds + rs * XSLOT) + uniform(wn) * 64 + lane;
+    const int N = p.N;
+    const int nend = min(N, it.n0 + 64 * it.w);
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+    for (int i0 = 0; i0 < MB; i0 += MBP) {
+      __syncthreads();  // every wave is past its last read of the slot
+      if (kh == 1) {
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          if (i < MBA) red_a[(j * MBA + i) * 256] = acc[j][i];
-          else red_b[(j * MBA + i - MBA) * 256] = acc[j][i];
-        }
-    }
-    __syncthreads();
-    if (kh == 0) {
-      const int N = p.N;
-      const int nend = min(N, it.n0 + 64 * it.w);
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int m = i * 16 + r16;
-        if (m < it.rows) {
-          uint16_t* crow = p.C + (size_t)(it.row0 + m) * N;
+          for (int i = i0; i < MB && i < i0 + MBP; ++i) red[(j * MBP + i - i0) * 256] = acc[j][i];
+      }
+      __syncthreads();
+      if (kh == 0) {
 #pragma unroll
-          for (int j = 0; j < NBW; ++j) {
-            const int n = it.n0 + (wn * NBW + j) * 16 + q * 4;
-            const v4f o = i < MBA ? red_a[(j * MBA + i) * 256] : red_b[(j * MBA + i - MBA) * 256];
-            if (n < nend) store_bf16x4(crow + n, acc[j][i] + o);
+        for (int i = i0; i < MB && i < i0 + MBP; ++i) {
+          const int m = i * 16 + r16;
+          if (m < it.rows) {
+            uint16_t* crow = p.C + (size_t)(it.row0 + m) * N;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              const int n = it.n0 + (wn * NBW + j) * 16 + q * 4;
+              const v4f o = red[(j * MBP + i - i0) * 256];
+              if (n < nend) store_bf16x4(crow + n, acc[j][i] + o);
+            }
           }
         }
       }
     }
-    __syncthreads();  // the two regions are reloaded next
   }
 
   template <class Source>
@@ -710,12 +737,14 @@ struct StreamRun {
         for (int j = 0; j < NBW; ++j) wr[u][kg][j] = v4i{0, 0, 0, 0};
     const int SE = S + (S & 1);  // stages run per item (even)
     const int C = SE / 2;        // scale chunks per item (two stages each)
+    uint32_t xo[MB], wo[2][NBW];
+    offsets(cur, xo, wo);
     // prologue of the first item: scale chunk 0, stages 0 and 1
     issue_scales(cur, 0, 0);
-    issue_x(cur, 0, 0, true);
-    issue_w(cur, 0, wr[0], true);
-    issue_x(cur, 1, 1, true);
-    issue_w(cur, 1, wr[1], true);
+    issue_x(cur, xo, 0, 0, true);
+    issue_w(cur, wo, 0, wr[0], true);
+    issue_x(cur, xo, 1, 1, true);
+    issue_w(cur, wo, 1, wr[1], true);
     int t = 0;      // global stage of the workgroup's pipeline
     int base = 0;   // global chunk number of the item's chunk 0
     for (;;) {
@@ -724,46 +753,63 @@ struct StreamRun {
       for (int j = 0; j < NBW; ++j)
 #pragma unroll
         for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-      // a stand-in with valid addresses for the loads of a missing next item
-      const StreamWork nx = nxt.valid ? nxt : cur;
-      // item stage s uses register slot s & 1: items run an even number of
-      // stages (an odd count gets one more, without MFMAs, whose loads are
-      // issued with exec = 0), so every item starts on slot 0 and the loop
-      // has one body -- the ring registers keep their places and are never
-      // copied while their loads are in flight
+      // the next item (or, when there is none, the current one as a stand-in
+      // with valid addresses for loads issued with exec = 0) and its offsets
+      const StreamWork nx = pick(nxt.valid, nxt, cur);
+      uint32_t nxo[MB], nwo[2][NBW];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) nxo[i] = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) nwo[h][j] = 0;
+      bool have_next_offsets = false;
       auto stage = [&](int s, int u) __attribute__((always_inline)) {
         stage_wait(wr[u]);
-        // the loads this stage issues, for stage sn = s + 2: the item's own
-        // stage, the next item's stage 0 (sn == SE), or none (exec = 0: the
-        // padding stage, the last stage, a missing next item).  One load
-        // site per ring register, with no branch around it, so that the
-        // register is one value the compiler never copies.
+        // the loads of stage sn = s + 2: the item's own stage, the next
+        // item's stage 0 or 1, or nothing (exec = 0: the padding stage, a
+        // missing next item).  One load site per ring register, with no
+        // branch around it.
         const int sn = s + 2;
-        const bool own = sn < S, next0 = sn == SE;
-        const StreamWork wi = own ? cur : nx;
-        const int ws = own ? sn : 0;
-        const bool live = own || (next0 && nxt.valid);
+        const bool own = sn < S, pad = sn >= S && sn < SE;
+        const bool next = sn >= SE;
+        if (next && !have_next_offsets) {
+          offsets(nx, nxo, nwo);
+          have_next_offsets = true;
+        }
+        const StreamWork wi = pick(next, nx, cur);
+        const int ws = own ? sn : (pad ? S - 1 : sn - SE);
+        const bool live = own || (next && nxt.valid);
+        uint32_t lxo[MB], lwo[2][NBW];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) lxo[i] = next ? nxo[i] : xo[i];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) lwo[h][j] = next ? nwo[h][j] : wo[h][j];
         if (own && (sn & 1) == 0) issue_scales(cur, sn >> 1, (base + (sn >> 1)) & 1);
-        issue_x(wi, ws, (t + 2) % NX, live);
+        if (sn == SE && nxt.valid) issue_scales(nx, 0, (base + C) & 1);
+        issue_x(wi, lxo, ws, (t + 2) % NX, live);
         if (s < S) compute(s, t % NX, (base + (s >> 1)) & 1, wr[u], acc);
-        issue_w(wi, ws, wr[u], live);
+        issue_w(wi, lwo, ws, wr[u], live);
         ++t;
       };
       for (int s = 0; s < SE; s += 2) {
         stage(s, 0);
         stage(s + 1, 1);
       }
-      // t is now one past the item's last stage: its slot (t - 1) % 3 and
-      // slot (t + 1) % 3 are free; slot t % 3 holds the next item's stage 0
-      reduce_store(cur, (t + 2) % NX, (t + 1) % NX, acc);
+      // t is one past the item's last stage: slots t % 3 and (t + 1) % 3
+      // hold the next item's first two stages, slot (t + 2) % 3 is free
+      reduce_store(cur, (t + 2) % NX, acc);
       if (!nxt.valid) break;
-      // the next item's scale chunk 0 and stage 1, after the stores
-      const int nbase = base + C;
-      issue_scales(nxt, 0, nbase & 1);
-      issue_x(nxt, 1, (t + 1) % NX, true);
-      issue_w(nxt, 1, wr[1], true);
-      base = nbase;
+      base += C;
       cur = nxt;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) xo[i] = nxo[i];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) wo[h][j] = nwo[h][j];
       nxt = src.next();
     }
     // every load has retired; the ties keep the ring registers reserved until here
@@ -782,9 +828,8 @@ struct StreamRun {
 // a share of the workgroups proportional to its cost, units x (6 + MB) (a
 // 64-column unit streams 6 KB of weights per stage against MB KB of
 // activation rows), with at least one workgroup for a class that has tiles;
-// inside a class, workgroup b' of G_c streams the contiguous units
-// [U_c b' / G_c, U_c (b' + 1) / G_c) of the class's U_c = tiles x units
-// (a range may cross from one expert to the next; an item never does).
+// inside a class the units are split by stream_range (an item never
+// crosses experts).
 //   s_eord[k]    expert at class-ordered position k
 //   s_cls[c]     class c: {tiles, first position, first workgroup, workgroups}
 // Wave 0 fills them; every thread must call it.
@@ -903,8 +948,11 @@ __device__ __forceinline__ void stream_phase_continuous(const GemmArgs& p, uint8
   }
   if (c < 0) return;
   const int tiles = uniform(s_cls[c][0]), gn = uniform(s_cls[c][3]), bl = b - uniform(s_cls[c][2]);
-  const long long U = (long long)tiles * nu;
-  StreamRangeSource src{s_off, s_eord, uniform(s_cls[c][1]), nu, P1_RANGE_MAXNBW, U * bl / gn, U * (bl + 1) / gn};
+  // inside the class, the split of stream_range: fewer tiles than
+  // workgroups -> each tile its own workgroups (no range crosses experts)
+  long long u0 = 0, u1 = 0;
+  stream_range(tiles, nu, bl, gn, &u0, &u1);
+  StreamRangeSource src{s_off, s_eord, uniform(s_cls[c][1]), nu, P1_RANGE_MAXNBW, u0, u1};
   switch (c) {
     case 0: StreamRun<P1_RANGE_MAXNBW, 1>(p, lds, R).run(src); break;
     case 1: StreamRun<P1_RANGE_MAXNBW, 2>(p, lds, R).run(src); break;
