@@ -48,11 +48,7 @@ grouped_gemm_kernel(GemmArgs p) {
   if constexpr (!FUSED) {
     const int tiles = uniform(s_sbase[p.E]);
     const int nu = (p.N + 63) / 64;
-    const int G = p.K >> 7, S = ((G + 1) / 2 + P1_KG - 1) / P1_KG;   // stages per item
-    if (tiles > 0 && S >= 2) {
-      // one pipeline over all of the workgroup's items
-      stream_phase_continuous(p, lds, s_off, s_eord, s_rrc, R);
-    } else if (tiles > 0 && uniform(s_info[1]) == uniform(s_info[2]) &&
+    if (tiles > 0 && uniform(s_info[1]) == uniform(s_info[2]) &&
         (long long)tiles * nu >= 2LL * gridDim.x) {
       // every streaming tile has the same row blocks, so every 64-column unit
       // costs the same: an equal share of units per workgroup (with fewer

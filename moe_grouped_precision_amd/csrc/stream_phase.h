@@ -238,6 +238,9 @@ struct StreamItem {
       v4i wop[KG][NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) pair_operands(wr[u][0][j], wr[u][1][j], wop[0][j], wop[1][j]);
+      // the ring slot is free once paired: its next loads go out before the
+      // MFMAs, so two stages stay in flight while this one computes
+      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G, sn < S);
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         const int gl = s * KG + kg;  // group index within this wave's half
@@ -264,7 +267,6 @@ struct StreamItem {
           }
         }
       }
-      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G, sn < S);
     };
 
     static_assert(D == 2, "the stage loop below is written for two stages in flight");
@@ -483,482 +485,5 @@ __device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid,
   }
 }
 
-
-// ---------------------------------------------------------------------------
-// Continuous streaming: all of a workgroup's streaming items as one pipeline.
-//
-// The per-item schedule above fills its two-stage pipeline at the start of
-// every item and drains it at the end.  Here a workgroup runs a sequence of
-// items of one row-block count MB (the same register ring shape) back to
-// back, and the pipeline does not stop between them: stage s of an item
-// issues the loads of stage s + 2, and past the item's end those are the
-// next item's stages 0 and 1 (its scale chunk 0 with stage 0).  So when an
-// item's last stage has run, the next item's first two stages are already
-// on the way, and only the addition of the item's K halves (through the one
-// activation-ring slot no load is filling: the last stage's) separates the
-// two.  Items run an even number of stages (an odd count gets one more,
-// without MFMAs, whose loads are issued with exec = 0), so stage s always
-// uses register slot s & 1 and the loop has one body: the ring registers
-// keep their places and are never copied while their loads are in flight.
-// Every stage issues exactly one stage's worth of loads from one branch-free
-// site per register (exec = 0 where there is nothing to load), so every
-// wait is the same constant; the bf16 stores of a reduction, issued after
-// the next item's loads, only make the next two waits also wait for them.
-// Scale chunks alternate between two buffers by a chunk count kept across
-// items.  Items need at least two stages (K >= 640).  Numerics are those
-// of the per-item schedule (the same groups in the same order, the halves
-// added half 0 + half 1), so results do not depend on which schedule ran.
-// ---------------------------------------------------------------------------
-struct StreamWork {  // expert e, rows [row0, row0 + rows), columns n0 .. n0 + 64 w - 1
-  int e, row0, rows, n0, w;
-  bool valid;
-};
-
-// c ? a : b field by field (a whole-struct select makes the compiler pick
-// between the two objects' addresses, i.e. keep them in memory).
-__device__ __forceinline__ StreamWork pick(bool c, const StreamWork& a, const StreamWork& b) {
-  StreamWork r;
-  r.e = c ? a.e : b.e;
-  r.row0 = c ? a.row0 : b.row0;
-  r.rows = c ? a.rows : b.rows;
-  r.n0 = c ? a.n0 : b.n0;
-  r.w = c ? a.w : b.w;
-  r.valid = c ? a.valid : b.valid;
-  return r;
-}
-
-template <int NBW, int MB>
-struct StreamRun {
-  static constexpr int KG = P1_KG, D = 2, NX = 3;
-  static constexpr int XSLOT = KG * P1_XGROUP;
-  static constexpr int PER = KG * (NBW + MB);   // loads per wave per stage
-  static constexpr int WIDTH = 64 * NBW;
-  static constexpr int SBS = stream_sb_stride(NBW);
-  static constexpr int SAB = P1_SB + 2 * SBS;
-  // row blocks added per pass of the reduction through one ring slot
-  static constexpr int MBP = (8 / NBW) < MB ? (8 / NBW) : MB;
-  static_assert(KG == 2 && D == 2, "written for two groups per stage and two stages in flight");
-  static_assert(NX * XSLOT <= P1_XRING, "activation ring");
-  static_assert(NBW * MBP * 4 * 1024 <= XSLOT && MBP >= 1, "a reduction pass fits one ring slot");
-  static_assert(SBS >= 2 * 64 * NBW * SC * 4 && SAB + 2 * P1_SABUF <= P1_BYTES, "scale chunk buffers");
-  static_assert((D - 1) * PER < 64, "vmcnt range");
-  static_assert(NBW <= stream_max_nbw(MB), "register budget");
-
-  const GemmArgs& p;
-  uint8_t* lds;
-  int R, G, Gh, S, kh, wn, gbase, gcount;
-
-  __device__ __forceinline__ StreamRun(const GemmArgs& p_, uint8_t* lds_, int R_) : p(p_), lds(lds_), R(R_) {
-    const int wave = threadIdx.x >> 6;
-    G = p.K >> 7;
-    Gh = (G + 1) / 2;
-    S = (Gh + KG - 1) / KG;
-    kh = uniform(wave >> 2);
-    wn = uniform(wave & 3);
-    gbase = kh ? Gh : 0;
-    gcount = kh == 0 ? Gh : G - Gh;
-  }
-
-  // This lane's offsets of an item: activation rows (row clamped to the
-  // item's rows, 16-byte chunk swizzled) and weight columns (clamped to N).
-  __device__ __forceinline__ void offsets(const StreamWork& it, uint32_t (&xo)[MB], uint32_t (&wo)[2][NBW]) const {
-    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
-    const int q = lane >> 4, r16 = lane & 15;
-    const int K = p.K, N = p.N;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int jx = wave * MB + i;
-      const int quad = jx % (4 * MB);
-      const int r = quad * 4 + (lane >> 3);
-      xo[i] = (uint32_t)min(r, it.rows - 1) * (uint32_t)K + (((lane & 7) ^ (r & 7)) << 4);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int n = min(it.n0 + (wn * NBW + j) * 16 + 8 * h + (r16 & 7), N - 1);
-        wo[h][j] = (uint32_t)(n - it.n0) * (uint32_t)(K >> 1) + q * 16;
-      }
-  }
-
-  // Activation rows of item stage s into ring slot `slot` (2 groups x 2
-  // halves x 64 rows x 128 B; MB loads of 4 rows per wave and group, lanes
-  // 0-31 load).
-  __device__ __forceinline__ void issue_x(const StreamWork& it, const uint32_t (&xo)[MB], int s, int slot,
-                                          bool live) const {
-    const int wave = uniform(threadIdx.x >> 6);
-    const uint8_t* xt = p.A + (size_t)it.row0 * p.K;
-    const uint64_t mask = live_mask(live) & 0xffffffffull;
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      const int g0 = min(s * KG + kg, G - 1), g1 = min(Gh + s * KG + kg, G - 1);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int jx = wave * MB + i;
-        const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
-        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
-                 lds_u32(lds + slot * XSLOT + kg * P1_XGROUP + h * 8192 + quad * 512), mask);
-      }
-    }
-  }
-
-  // Weights of item stage s for this wave (the layout of StreamItem::load_w);
-  // blocks outside the item's width load nothing.
-  __device__ __forceinline__ void issue_w(const StreamWork& it, const uint32_t (&wo)[2][NBW], int s,
-                                          v4i (&w)[KG][NBW], bool live) const {
-    const int r16 = opaque_lane() & 15;
-    const uint8_t* wt = p.B + ((size_t)it.e * p.N + it.n0) * (size_t)(p.K >> 1);
-    const uint32_t goff = (uint32_t)min(gbase + s * KG + (r16 >> 3), G - 1) * 64u;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int b16 = uniform((wn * NBW + j) * 16);
-        vm_load16_nt(w[h][j], wt, wo[h][j] + goff, live_mask(live && b16 < 64 * it.w));
-      }
-  }
-
-  // Scale chunk c of an item (groups SC c .. SC c + 3 of each half) into buffer buf.
-  __device__ __forceinline__ void issue_scales(const StreamWork& it, int c, int buf) const {
-    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
-    const int K = p.K, N = p.N;
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-      const int idx = (wave * NBW + i) * 64 + lane;  // [h][col][gg]
-      const int h = idx / (WIDTH * SC), rem = idx - h * (WIDTH * SC);
-      const int col = rem >> 2, gg = rem & 3;
-      const int n = min(it.n0 + col, N - 1);
-      const int g = min((h ? Gh : 0) + SC * c + gg, G - 1);
-      vm_dma4(p.SB + ((size_t)it.e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-              lds_u32(lds + P1_SB + buf * SBS + (wave * NBW + i) * 256));
-    }
-    const int idx = wave * 64 + lane;  // [h][row][gg]
-    const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
-    const size_t row = (size_t)it.row0 + min(r, it.rows - 1);
-    const int g = min((h ? Gh : 0) + SC * c + gg, G - 1);
-    vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + SAB + buf * P1_SABUF + wave * 256));
-  }
-
-  // The MFMAs and promotions of item stage s.
-  __device__ __forceinline__ void compute(int s, int xslot, int sbuf, const v4i (&w)[KG][NBW],
-                                          v4f (&acc)[NBW][MB]) const {
-    const int lane = opaque_lane();
-    const int q = lane >> 4, r16 = lane & 15;
-    const uint8_t* slot = lds + xslot * XSLOT;
-    const uint8_t* sbb = lds + P1_SB + sbuf * SBS;
-    const uint8_t* sab = lds + SAB + sbuf * P1_SABUF;
-    v4i wop[KG][NBW];
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) StreamItem<NBW, KG, MB>::pair_operands(w[0][j], w[1][j], wop[0][j], wop[1][j]);
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      const int gl = s * KG + kg;  // group index within this wave's half
-      if (gl < gcount) {
-        const int gg = gl % SC;
-        int sbv[NBW];
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int col = (wn * NBW + j) * 16 + r16;
-          sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
-        }
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int m = i * 16 + r16;
-          const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
-          const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
-          const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
-          const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
-#pragma unroll
-          for (int j = 0; j < NBW; ++j) promote(acc[j][i], sa, mfma_group(wop[kg][j], x0, x1, sbv[j]));
-        }
-      }
-    }
-  }
-
-  // Wait for the weights of the stage about to run (exactly one later stage's
-  // loads may be in flight, or stores older than them), make them readable,
-  // meet the other waves.
-  __device__ __forceinline__ static void stage_wait(v4i (&w)[KG][NBW]) {
-    wait_vm<(D - 1) * PER>();
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) tie(w[kg][j]);
-    wg_barrier();
-  }
-
-  // Add the K halves of an item through ring slot rs, MBP row blocks per
-  // pass, and store the bf16 result.
-  __device__ __forceinline__ void reduce_store(const StreamWork& it, int rs, v4f (&acc)[NBW][MB]) const {
-    const int lane = opaque_lane();
-    const int q = lane >> 4, r16 = lane & 15;
-    v4f* red = reinterpret_cast<v4f*>(lds + rs * XSLOT) + uniform(wn) * 64 + lane;
-    const int N = p.N;
-    const int nend = min(N, it.n0 + 64 * it.w);
-#pragma unroll
-    for (int i0 = 0; i0 < MB; i0 += MBP) {
-      __syncthreads();  // every wave is past its last read of the slot
-      if (kh == 1) {
-#pragma unroll
-        for (int j = 0; j < NBW; ++j)
-#pragma unroll
-          for (int i = i0; i < MB && i < i0 + MBP; ++i) red[(j * MBP + i - i0) * 256] = acc[j][i];
-      }
-      __syncthreads();
-      if (kh == 0) {
-#pragma unroll
-        for (int i = i0; i < MB && i < i0 + MBP; ++i) {
-          const int m = i * 16 + r16;
-          if (m < it.rows) {
-            uint16_t* crow = p.C + (size_t)(it.row0 + m) * N;
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-              const int n = it.n0 + (wn * NBW + j) * 16 + q * 4;
-              const v4f o = red[(j * MBP + i - i0) * 256];
-              if (n < nend) store_bf16x4(crow + n, acc[j][i] + o);
-            }
-          }
-        }
-      }
-    }
-  }
-
-  template <class Source>
-  __device__ __forceinline__ void run(Source& src) {
-    StreamWork cur = src.next();
-    if (!cur.valid) return;
-    StreamWork nxt = src.next();
-    v4i wr[D][KG][NBW];
-#pragma unroll
-    for (int u = 0; u < D; ++u)
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) wr[u][kg][j] = v4i{0, 0, 0, 0};
-    const int SE = S + (S & 1);  // stages run per item (even)
-    const int C = SE / 2;        // scale chunks per item (two stages each)
-    uint32_t xo[MB], wo[2][NBW];
-    offsets(cur, xo, wo);
-    // prologue of the first item: scale chunk 0, stages 0 and 1
-    issue_scales(cur, 0, 0);
-    issue_x(cur, xo, 0, 0, true);
-    issue_w(cur, wo, 0, wr[0], true);
-    issue_x(cur, xo, 1, 1, true);
-    issue_w(cur, wo, 1, wr[1], true);
-    int t = 0;      // global stage of the workgroup's pipeline
-    int base = 0;   // global chunk number of the item's chunk 0
-    for (;;) {
-      v4f acc[NBW][MB];
-#pragma unroll
-      for (int j = 0; j < NBW; ++j)
-#pragma unroll
-        for (int i = 0; i < MB; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-      // the next item (or, when there is none, the current one as a stand-in
-      // with valid addresses for loads issued with exec = 0) and its offsets
-      const StreamWork nx = pick(nxt.valid, nxt, cur);
-      uint32_t nxo[MB], nwo[2][NBW];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) nxo[i] = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) nwo[h][j] = 0;
-      bool have_next_offsets = false;
-      auto stage = [&](int s, int u) __attribute__((always_inline)) {
-        stage_wait(wr[u]);
-        // the loads of stage sn = s + 2: the item's own stage, the next
-        // item's stage 0 or 1, or nothing (exec = 0: the padding stage, a
-        // missing next item).  One load site per ring register, with no
-        // branch around it.
-        const int sn = s + 2;
-        const bool own = sn < S, pad = sn >= S && sn < SE;
-        const bool next = sn >= SE;
-        if (next && !have_next_offsets) {
-          offsets(nx, nxo, nwo);
-          have_next_offsets = true;
-        }
-        const StreamWork wi = pick(next, nx, cur);
-        const int ws = own ? sn : (pad ? S - 1 : sn - SE);
-        const bool live = own || (next && nxt.valid);
-        uint32_t lxo[MB], lwo[2][NBW];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) lxo[i] = next ? nxo[i] : xo[i];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < NBW; ++j) lwo[h][j] = next ? nwo[h][j] : wo[h][j];
-        if (own && (sn & 1) == 0) issue_scales(cur, sn >> 1, (base + (sn >> 1)) & 1);
-        if (sn == SE && nxt.valid) issue_scales(nx, 0, (base + C) & 1);
-        issue_x(wi, lxo, ws, (t + 2) % NX, live);
-        if (s < S) compute(s, t % NX, (base + (s >> 1)) & 1, wr[u], acc);
-        issue_w(wi, lwo, ws, wr[u], live);
-        ++t;
-      };
-      for (int s = 0; s < SE; s += 2) {
-        stage(s, 0);
-        stage(s + 1, 1);
-      }
-      // t is one past the item's last stage: slots t % 3 and (t + 1) % 3
-      // hold the next item's first two stages, slot (t + 2) % 3 is free
-      reduce_store(cur, (t + 2) % NX, acc);
-      if (!nxt.valid) break;
-      base += C;
-      cur = nxt;
-#pragma unroll
-      for (int i = 0; i < MB; ++i) xo[i] = nxo[i];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) wo[h][j] = nwo[h][j];
-      nxt = src.next();
-    }
-    // every load has retired; the ties keep the ring registers reserved until here
-    wait_vm<0>();
-#pragma unroll
-    for (int u = 0; u < D; ++u)
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) tie(wr[u][kg][j]);
-  }
-};
-
-// Work split for the continuous pipeline.  The streaming experts are grouped
-// by row blocks (MB = 1..4, one register ring shape each); every class gets
-// a share of the workgroups proportional to its cost, units x (6 + MB) (a
-// 64-column unit streams 6 KB of weights per stage against MB KB of
-// activation rows), with at least one workgroup for a class that has tiles;
-// inside a class the units are split by stream_range (an item never
-// crosses experts).
-//   s_eord[k]    expert at class-ordered position k
-//   s_cls[c]     class c: {tiles, first position, first workgroup, workgroups}
-// Wave 0 fills them; every thread must call it.
-__device__ __forceinline__ void stream_class_plan(const int* s_off, int E, int nu, int grid, int* s_eord,
-                                                  int (*s_cls)[4]) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (E + 63) / 64;
-    const int i0 = lane * per;
-    int cnt[4] = {0, 0, 0, 0};
-    for (int k = 0; k < per; ++k) {
-      const int e = i0 + k;
-      if (e < E) {
-        const int rows = s_off[e + 1] - s_off[e];
-        if (rows > 0 && rows <= S_MAX) {
-          const int c = (rows - 1) >> 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) cnt[j] += j == c;
-        }
-      }
-    }
-    int pre[4], tot[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int incl = wave_inclusive_sum(cnt[j]);
-      pre[j] = incl - cnt[j];
-      tot[j] = __builtin_amdgcn_readlane(incl, 63);
-    }
-    int pos0[4], nonempty = 0;
-    double cost[4], total = 0.0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pos0[j] = j == 0 ? 0 : pos0[j - 1] + tot[j - 1];
-      cost[j] = (double)tot[j] * nu * (6 + j + 1);
-      total += cost[j];
-      nonempty += tot[j] > 0;
-    }
-    // one workgroup per nonempty class, the rest by cumulative cost
-    const int rest = grid - nonempty;
-    int g0[4], gn[4];
-    double cum = 0.0;
-    int given = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lo = (int)((double)rest * cum / total);
-      cum += cost[j];
-      const int hi = j == 3 ? rest : (int)((double)rest * cum / total);
-      g0[j] = given + lo;
-      gn[j] = tot[j] > 0 ? 1 + hi - lo : 0;
-      given += tot[j] > 0 ? 1 : 0;
-    }
-    int next[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) next[j] = pos0[j] + pre[j];
-    for (int k = 0; k < per; ++k) {
-      const int e = i0 + k;
-      if (e < E) {
-        const int rows = s_off[e + 1] - s_off[e];
-        if (rows > 0 && rows <= S_MAX) {
-          const int c = (rows - 1) >> 4;
-          int pos = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (j == c) pos = next[j]++;
-          s_eord[pos] = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane == j) {
-        s_cls[j][0] = tot[j];
-        s_cls[j][1] = pos0[j];
-        s_cls[j][2] = g0[j];
-        s_cls[j][3] = gn[j];
-      }
-  }
-  __syncthreads();
-}
-
-// The items of one workgroup's range of a class: [u, u_end) over the class's
-// tiles (class-ordered experts from pos0), at most W units per item and
-// never across an expert boundary.
-struct StreamRangeSource {
-  const int* s_off;
-  const int* s_eord;
-  int pos0, nu, W;
-  long long u, u_end;
-  __device__ __forceinline__ StreamWork next() {
-    StreamWork it{0, 0, 0, 0, 0, false};
-    if (u >= u_end) return it;
-    const int k = (int)(u / nu);
-    const int c0 = (int)(u - (long long)k * nu);
-    it.w = (int)min((long long)min(W, nu - c0), u_end - u);
-    it.e = uniform(s_eord[pos0 + k]);
-    it.row0 = uniform(s_off[it.e]);
-    it.rows = uniform(s_off[it.e + 1]) - it.row0;
-    it.n0 = c0 * 64;
-    it.valid = true;
-    u += it.w;
-    return it;
-  }
-};
-
-// Streaming phase of one workgroup with the continuous pipeline (K >= 640).
-__device__ __forceinline__ void stream_phase_continuous(const GemmArgs& p, uint8_t* lds, const int* s_off,
-                                                        int* s_eord, int (*s_cls)[4], int R) {
-  const int nu = (p.N + 63) / 64;
-  stream_class_plan(s_off, p.E, nu, gridDim.x, s_eord, s_cls);
-  const int b = blockIdx.x;
-  int c = -1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int g0 = uniform(s_cls[j][2]), gn = uniform(s_cls[j][3]);
-    if (b >= g0 && b < g0 + gn) c = j;
-  }
-  if (c < 0) return;
-  const int tiles = uniform(s_cls[c][0]), gn = uniform(s_cls[c][3]), bl = b - uniform(s_cls[c][2]);
-  // inside the class, the split of stream_range: fewer tiles than
-  // workgroups -> each tile its own workgroups (no range crosses experts)
-  long long u0 = 0, u1 = 0;
-  stream_range(tiles, nu, bl, gn, &u0, &u1);
-  StreamRangeSource src{s_off, s_eord, uniform(s_cls[c][1]), nu, P1_RANGE_MAXNBW, u0, u1};
-  switch (c) {
-    case 0: StreamRun<P1_RANGE_MAXNBW, 1>(p, lds, R).run(src); break;
-    case 1: StreamRun<P1_RANGE_MAXNBW, 2>(p, lds, R).run(src); break;
-    case 2: StreamRun<P1_RANGE_MAXNBW, 3>(p, lds, R).run(src); break;
-    default: StreamRun<P1_RANGE_MAXNBW, 4>(p, lds, R).run(src); break;
-  }
-}
 
 }  // namespace w4a8

@@ -188,17 +188,17 @@ DECODE_ROWS = [0, 0, 1, 3, 5, 5, 6, 6, 7, 7, 7, 8, 9, 9, 11, 14, 15, 15, 16, 17,
     # narrower last item per expert (62 units) or a half unit at N (4000)
     (DECODE_ROWS, 3968, 256),
     (DECODE_ROWS, 4000, 128),
-    # K >= 640: the streaming phase runs each workgroup's items as one
-    # pipeline, experts grouped by row blocks (two to seven stages per item,
-    # odd and even stage counts, a kh=1 half one group short, narrow last
-    # items, ranges crossing expert boundaries)
+    # longer K loops (two to seven stages per item, odd and even stage
+    # counts, a kh=1 half one group short at K = 640, narrow last items of 62
+    # and 33 units per expert, two and more items per workgroup)
     (DECODE_ROWS, 3968, 768),
+    (DECODE_ROWS, 3968, 640),
+    ([64, 1, 17, 33, 49, 0, 16, 32, 48] * 7, 2112, 1792),
     (DECODE_ROWS, 4000, 1408),
     ([5] * 300, 192, 1024),
     ([40] * 3 + [0] + [33] * 2, 8192, 640),
     (list(range(0, 140, 7)), 256, 1152),
     ([3], 32, 896),
-    ([64, 1, 17, 33, 49, 0, 16, 32, 48] * 7, 2112, 1792),
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
