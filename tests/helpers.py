@@ -32,7 +32,8 @@ MAX_ULP_LARGE = 1          # bf16 ulps, on elements with |ref| >= rms(ref)
 # times N(0, 0.02) MXFP4 weights, whose products span about a dozen
 # binades, 1.1e-6 at most over every workload (2^-19.8); random E4M3 x E2M1
 # codes with E8M0 scales over 20 binades, whose products span about 40
-# binades, 7.5e-5 (2^-13.7).  The bounds keep a 16x margin over both.
+# binades, 2.1e-4 (2^-12.2) at most over the edge-case shapes.  The bounds
+# keep a margin of 16x and 4.7x over them.
 GROUP_EPS_QUANTIZED = 2.0 ** -16
 GROUP_EPS_RANDOM_CODES = 2.0 ** -10
 
