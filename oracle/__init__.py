@@ -26,6 +26,9 @@ Modules:
   combine -- top-k weighted sum of grouped output rows back to tokens.
   swiglu  -- silu(gate) * up of the gate/up output, requantized to E4M3, in
              fp64, and the admissibility check of an fp32 result against it.
+  a16     -- the grouped GEMM with bf16 activations and FP4 weights, MXFP4
+             (E8M0 per 32) or NVFP4 (E4M3 per 16 and one fp32 scale per
+             expert) scales.
 
 Parity status: no page prints a worked example or output value for any of
 these, so every function is pinned by closed forms, invariants, exact
@@ -47,3 +50,4 @@ from .route import route_ref  # noqa: F401
 from .quant import bf16_bits_to_f32, e4m3_encode_rne, quantize_gather, quantize_tokens  # noqa: F401
 from .combine import combine_ref  # noqa: F401
 from .swiglu import check_h_quant, check_swiglu_quant, h_quant_f64, silu_f64, swiglu_f64, swiglu_quant_f64  # noqa: F401
+from .a16 import FMT_MX, FMT_NV, grouped_gemm_a16_bf16, grouped_gemm_a16_f64  # noqa: F401

@@ -246,3 +246,73 @@ def random_codes_problem(counts, N: int, K: int, seed: int, sb_lo: int = 112, sb
     offsets = torch.zeros(E + 1, dtype=torch.int32)
     offsets[1:] = torch.cumsum(torch.tensor(list(counts), dtype=torch.int64), 0).to(torch.int32)
     return A, SA, B, SB, offsets
+
+
+def quantize_nvfp4(w: torch.Tensor):
+    """fp32 [N, K] -> (packed E2M1 uint8 [N, K/2], E4M3 codes uint8 [N, K/16],
+    fp32 tensor scale gs): gs = amax|w| / (448 * 6), each 16-block's E4M3
+    code the RNE of amax_block / (6 gs), then the E2M1 RNE of w / (scale gs)."""
+    N, K = w.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    amax = float(w.abs().max())
+    gs = torch.tensor(amax / (448.0 * 6.0) if amax > 0 else 1.0, dtype=torch.float32)
+    wb = w.reshape(N, K // 16, 16)
+    bamax = wb.abs().amax(dim=2)
+    sc = (bamax / (6.0 * gs)).clamp(max=448.0).to(torch.float8_e4m3fn)
+    dec = sc.to(torch.float32)
+    dec = torch.where(dec > 0, dec, torch.ones_like(dec))
+    y = wb / (dec * gs).unsqueeze(2)
+    codes = _e2m1_codes(y).reshape(N, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+    return packed, sc.view(torch.uint8).contiguous(), float(gs)
+
+
+def bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    """fp32 -> bf16 (torch's round to nearest even), as uint16-viewable int16."""
+    return x.to(torch.bfloat16).view(torch.int16).contiguous()
+
+
+@dataclasses.dataclass
+class ProblemA16:
+    name: str
+    fmt: int                    # 0 MXFP4 (E8M0 per 32), 1 NVFP4 (E4M3 per 16 + fp32 per expert)
+    E: int
+    T: int
+    top_k: int
+    N: int
+    K: int
+    topk_ids: torch.Tensor      # int32 [T, top_k] (CPU)
+    A: torch.Tensor             # int16 [R, K] bf16 bits, grouped row order
+    B: torch.Tensor             # uint8 [E, N, K/2] packed E2M1
+    SB: torch.Tensor            # uint8 [E, N, K/32] E8M0 or [E, N, K/16] E4M3
+    GS: torch.Tensor            # fp32 [E] (ones for MXFP4)
+
+    @property
+    def R(self) -> int:
+        return self.T * self.top_k
+
+
+def make_a16_problem(name: str, fmt: int, device: str = "cpu", **overrides) -> ProblemA16:
+    """A workload of CONFIGS (shapes and routing) with bf16 activations
+    (N(0,1) rounded to bf16) and N(0, 0.02) weights quantized to MXFP4 or
+    NVFP4."""
+    cfg = dict(CONFIGS[name]) if name in CONFIGS else {}
+    cfg.update({k: v for k, v in overrides.items() if v is not None})
+    E_, T_, k_, N_, K_ = cfg["E"], cfg["T"], cfg["top_k"], cfg["N"], cfg["K"]
+    seed_ = cfg["seed"] + 101 + fmt
+    ids = make_routing(cfg["routing"], T_, E_, k_, cfg["seed"])
+    R = T_ * k_
+    ga = _gen(seed_, _S_A, device)
+    A = bf16_bits(torch.randn((R, K_), generator=ga, dtype=torch.float32, device=device))
+    gb = _gen(seed_, _S_B, device)
+    B = torch.empty((E_, N_, K_ // 2), dtype=torch.uint8, device=device)
+    SB = torch.empty((E_, N_, K_ // (32 if fmt == 0 else 16)), dtype=torch.uint8, device=device)
+    GS = torch.ones(E_, dtype=torch.float32, device=device)
+    for e in range(E_):
+        w = 0.02 * torch.randn((N_, K_), generator=gb, dtype=torch.float32, device=device)
+        if fmt == 0:
+            B[e], SB[e] = quantize_mxfp4(w)
+        else:
+            B[e], SB[e], GS[e] = quantize_nvfp4(w)
+    return ProblemA16(name, fmt, E_, T_, k_, N_, K_, ids, A, B, SB, GS)

@@ -79,3 +79,16 @@ def test_wide_routing_is_a_top_k_selection():
     u = torch.bincount(synth.make_wide_routing(2000, 2048, 8, 5).reshape(-1).long(), minlength=2048)
     w = torch.bincount(synth.make_wide_routing(2000, 2048, 8, 5, skew=True).reshape(-1).long(), minlength=2048)
     assert int(w.max()) > 4 * int(u.max())
+
+
+def test_nvfp4_quantizer_gives_valid_codes_and_a_positive_tensor_scale():
+    g = torch.Generator().manual_seed(8)
+    w = 0.02 * torch.randn((64, 256), generator=g)
+    B, SB, gs = synth.quantize_nvfp4(w)
+    assert B.shape == (64, 128) and SB.shape == (64, 16) and gs > 0
+    assert not torch.any((SB & 0x7F) == 0x7F)          # no NaN scale codes
+    assert not torch.any(SB & 0x80)                     # block scales are amaxes: no sign
+    p = synth.make_a16_problem("tiny", 1)
+    assert p.SB.shape == (p.E, p.N, p.K // 16) and torch.all(p.GS > 0)
+    p0 = synth.make_a16_problem("tiny", 0)
+    assert p0.SB.shape == (p0.E, p0.N, p0.K // 32) and torch.all(p0.GS == 1)
