@@ -64,6 +64,12 @@ enum {
   W4A8_SCALE_M_MAJOR = 1    /* a_scales fp32 [K/128][R]: SA(r,g) at g*R+r, R = offsets[E] */
 };
 
+/* Weight-scale formats of w4a8_grouped_gemm_a16. */
+enum {
+  W4A8_WSCALE_MX = 0,  /* MXFP4: E8M0 code per (expert, column, 32 K), value 2^(code-127) */
+  W4A8_WSCALE_NV = 1   /* NVFP4: E4M3FN code per (expert, column, 16 K) */
+};
+
 /* Limits of this version. */
 #define W4A8_MAX_EXPERTS 2048        /* grouped GEMM: per-expert tables live in LDS */
 #define W4A8_MAX_PREP_EXPERTS 65536  /* route prep and plan; the route prep's LDS fit
@@ -330,6 +336,46 @@ int w4a8_grouped_gemm_swiglu(const uint8_t* A_fp8_dev, const float* a_scales_dev
                              const uint8_t* B13_fp4_dev, const uint8_t* b13_scales_e8m0_dev,
                              const int32_t* expert_offsets_dev, int E, int I, int K, uint8_t* A2_fp8_dev,
                              float* a2_scales_dev, int a2_scale_layout, void* stream);
+
+/*
+ * w4a8_grouped_gemm_a16 -- the grouped-contiguous expert GEMM with 16-bit
+ * activations and FP4 weights: the MXFP4 / NVFP4 A16 paths (humming PR #58,
+ * "Summary": small-M FP4 paths exercised by MXFP4/NVFP4 A16; "H200
+ * performance": BF16 FP4 expert-GEMM sweeps, gate/up and down):
+ *
+ *   C[r, n] = bf16_rne( gs[e] * sum_k A[r, k] * e2m1(B[e, n, k]) * s(e, n, k) )
+ *
+ * A_bf16_dev         bf16 [R][K] activations, rows grouped by expert as for
+ *                    w4a8_grouped_gemm.  16-byte aligned.
+ * B_fp4_dev          uint8 [E][N][K/2] packed E2M1 (element 2j in the low
+ *                    nibble).  16-byte aligned.
+ * b_scales_dev       W4A8_WSCALE_MX: uint8 [E][N][K/32] E8M0 codes, s =
+ *                    2^(code-127) (0xFF NaN); W4A8_WSCALE_NV: uint8
+ *                    [E][N][K/16] E4M3FN codes, s their value (0x7F/0xFF
+ *                    NaN).  4-byte aligned.
+ * b_scale_format     W4A8_WSCALE_MX or W4A8_WSCALE_NV (W4A8_ERR_LAYOUT
+ *                    otherwise).
+ * expert_scales_dev  fp32 [E] per-expert scales gs (the NVFP4 tensor scale of
+ *                    each expert's weights), or NULL for all ones.  4-byte
+ *                    aligned.
+ * expert_offsets_dev int32 [E+1] as for w4a8_grouped_gemm; offsets that do
+ *                    not start at 0 or decrease make the kernel write nothing.
+ * C_bf16_dev         out bf16 [R][N]; only rows < R are written.  16-byte
+ *                    aligned.
+ * Numerics: the FP4 weights are converted to bf16 times their scale (exact
+ * for scales whose products stay inside fp32's normal range) and summed on
+ * the matrix core in fp32 (one rounding per 16 K); the result is multiplied
+ * by gs[e] in fp32 and rounded once to bf16 (round to nearest even).  NaN
+ * scale codes make their columns NaN for the expert's rows.
+ * Limits: 1 <= E <= W4A8_MAX_PREP_EXPERTS; K % 128 == 0, 128 <= K <=
+ * W4A8_MAX_K; N % 16 == 0, 16 <= N <= W4A8_MAX_N; E * ceil(N/64) < 2^31.
+ * Every expert with rows is served, in passes of 64 rows over its weights
+ * (the schedule is tuned for small M: larger experts re-read their weights
+ * once per 64 rows).  No allocation, no host synchronisation.
+ */
+int w4a8_grouped_gemm_a16(const uint16_t* A_bf16_dev, const uint8_t* B_fp4_dev, const uint8_t* b_scales_dev,
+                          int b_scale_format, const float* expert_scales_dev, const int32_t* expert_offsets_dev,
+                          int E, int N, int K, uint16_t* C_bf16_dev, void* stream);
 
 /*
  * w4a8_plan_params -- the plan rule's constants, written to out_host[0..n-1]

@@ -17,14 +17,19 @@ torch when the caller does not pass them.
     grouped_gemm_planned_noalloc(A, SA, layout, B, SB, expert_offsets, out) -> out (plan in library scratch)
     grouped_gemm_swiglu(A, SA, layout, B13, SB13, expert_offsets, layout2)
                                      -> A2 (E4M3 codes of silu(gate) * up), SA2
+    grouped_gemm_a16(A_bf16, B, SB, fmt, expert_offsets, expert_scales=None, out=None)
+                                     -> C (bf16), MXFP4 (fmt 0) or NVFP4 (fmt 1) weights
 """
 
 from ._lib import (  # noqa: F401
     SCALE_M_MAJOR,
     SCALE_ROW_MAJOR,
+    WSCALE_MX,
+    WSCALE_NV,
     W4A8Error,
     combine,
     grouped_gemm,
+    grouped_gemm_a16,
     grouped_gemm_planned,
     grouped_gemm_planned_noalloc,
     grouped_gemm_swiglu,

@@ -48,6 +48,8 @@ def _declare(lib):
     lib.w4a8_grouped_gemm_planned_noalloc.restype = i32
     lib.w4a8_grouped_gemm_swiglu.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp]
     lib.w4a8_grouped_gemm_swiglu.restype = i32
+    lib.w4a8_grouped_gemm_a16.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp]
+    lib.w4a8_grouped_gemm_a16.restype = i32
     lib.w4a8_swiglu_quant.argtypes = [vp, i32, i32, vp, vp, i32, vp]
     lib.w4a8_swiglu_quant.restype = i32
     lib.w4a8_combine.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp, vp]
@@ -194,6 +196,46 @@ def grouped_gemm(A: torch.Tensor, SA: torch.Tensor, layout: int, B: torch.Tensor
         return out  # no rows: nothing to compute
     _check("w4a8_grouped_gemm", lib.w4a8_grouped_gemm(
         _ptr(A), _ptr(SA), int(layout), _ptr(B), _ptr(SB), _ptr(expert_offsets), E, N, K,
+        _ptr(out), _stream()))
+    return out
+
+
+WSCALE_MX = 0  # MXFP4 weight scales: E8M0 per 32 K
+WSCALE_NV = 1  # NVFP4 weight scales: E4M3 per 16 K
+
+
+def grouped_gemm_a16(A: torch.Tensor, B: torch.Tensor, SB: torch.Tensor, fmt: int, expert_offsets: torch.Tensor,
+                     expert_scales: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[R, N] (bf16) of the grouped GEMM with bf16 activations and FP4
+    weights.  A bf16 (or 16-bit integer bits) [R, K]; B uint8 [E, N, K/2]
+    packed E2M1; SB uint8 [E, N, K/32] E8M0 (fmt WSCALE_MX) or [E, N, K/16]
+    E4M3 (fmt WSCALE_NV); expert_scales fp32 [E] or None; expert_offsets
+    int32 [E+1] with offsets[E] == R."""
+    lib = load()
+    if A.dim() != 2 or B.dim() != 3 or SB.dim() != 3:
+        raise ValueError("A must be [R, K], B [E, N, K/2], SB [E, N, K/blk]")
+    R, K = A.shape
+    E, N, Kh = B.shape
+    blk = 32 if fmt == WSCALE_MX else 16
+    if Kh * 2 != K or SB.shape != (E, N, K // blk):
+        raise ValueError("inconsistent K between A, B and SB")
+    if A.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("A must be bfloat16 (or 16-bit integer bits)")
+    _need(A, "A", A.dtype)
+    _need(B, "B", torch.uint8)
+    _need(SB, "b_scales", torch.uint8)
+    if expert_scales is not None:
+        _need(expert_scales, "expert_scales", torch.float32, E)
+    _need(expert_offsets, "expert_offsets", torch.int32, E + 1)
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=A.device)
+    if out.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError("out must be bfloat16 (or 16-bit integer bits)")
+    _need(out, "out", out.dtype, R * N)
+    if R == 0:
+        return out
+    _check("w4a8_grouped_gemm_a16", lib.w4a8_grouped_gemm_a16(
+        _ptr(A), _ptr(B), _ptr(SB), int(fmt), _ptr(expert_scales), _ptr(expert_offsets), E, N, K,
         _ptr(out), _stream()))
     return out
 

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libw4a8.so")
-SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "quant.hip", "combine.hip"]
+SOURCES = ["api.cpp", "prep.hip", "gemm.hip", "quant.hip", "combine.hip", "a16.hip"]
 # roofline probes (sustained MFMA rate and HBM read bandwidth), a library of
 # their own: the benchmark loads them, the GEMM path does not
 PROBE_LIB = os.path.join(HERE, "libw4a8_probe.so")

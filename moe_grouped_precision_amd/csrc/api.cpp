@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -338,6 +339,36 @@ int w4a8_combine(const uint16_t* C_bf16_dev, int R, int N, const int32_t* row_of
   hipError_t e = w4a8::launch_combine(C_bf16_dev, R, N, row_of_slot_dev, weights_dev, T, top_k, out_bf16_dev,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A8_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int w4a8_grouped_gemm_a16(const uint16_t* A_bf16_dev, const uint8_t* B_fp4_dev, const uint8_t* b_scales_dev,
+                          int b_scale_format, const float* expert_scales_dev, const int32_t* expert_offsets_dev,
+                          int E, int N, int K, uint16_t* C_bf16_dev, void* stream) {
+  if (E < 1 || E > W4A8_MAX_PREP_EXPERTS)
+    return fail(W4A8_ERR_SHAPE, "E=%d outside [1, %d]", E, W4A8_MAX_PREP_EXPERTS);
+  if (K < 128 || K % 128 || K > W4A8_MAX_K)
+    return fail(W4A8_ERR_SHAPE, "K=%d must be a multiple of 128 in [128, %d]", K, W4A8_MAX_K);
+  if (N < 16 || N % 16 || N > W4A8_MAX_N)
+    return fail(W4A8_ERR_SHAPE, "N=%d must be a multiple of 16 in [16, %d]", N, W4A8_MAX_N);
+  if ((int64_t)E * ((N + 63) / 64) >= ((int64_t)1 << 31)) return fail(W4A8_ERR_SHAPE, "E * ceil(N/64) too large");
+  if (b_scale_format != W4A8_WSCALE_MX && b_scale_format != W4A8_WSCALE_NV)
+    return fail(W4A8_ERR_LAYOUT, "b_scale_format=%d is neither MXFP4 (0) nor NVFP4 (1)", b_scale_format);
+  if (!A_bf16_dev || !B_fp4_dev || !b_scales_dev || !expert_offsets_dev || !C_bf16_dev)
+    return fail(W4A8_ERR_NULL, "null pointer argument");
+  if (!aligned(A_bf16_dev, 16) || !aligned(B_fp4_dev, 16) || !aligned(C_bf16_dev, 16) ||
+      !aligned(b_scales_dev, 4) || !aligned(expert_scales_dev, 4) || !aligned(expert_offsets_dev, 4))
+    return fail(W4A8_ERR_ALIGN, "A, B, C need 16-byte and scales/offsets 4-byte alignment");
+  const DeviceInfo* d = nullptr;
+  int st = device_info(&d);
+  if (st != W4A8_OK) return st;
+  // items of (expert, 64 columns), about four workgroups of four waves per CU
+  const int64_t items = (int64_t)E * ((N + 63) / 64);
+  const int grid = (int)std::min<int64_t>(items, (int64_t)4 * d->cus);
+  hipError_t e = w4a8::launch_grouped_gemm_a16(A_bf16_dev, B_fp4_dev, b_scales_dev, b_scale_format,
+                                               expert_scales_dev, expert_offsets_dev, E, N, K, C_bf16_dev, grid,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "grouped_gemm_a16 launch: %s", hipGetErrorString(e));
   return ok();
 }
 

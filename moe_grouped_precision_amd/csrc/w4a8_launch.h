@@ -44,6 +44,9 @@ hipError_t launch_combine(const uint16_t* C, int R, int N, const int32_t* row_of
                           int top_k, uint16_t* out, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t* C, int R, int I, uint8_t* A, float* SA, int layout,
                                hipStream_t stream);
+hipError_t launch_grouped_gemm_a16(const uint16_t* A, const uint8_t* B, const uint8_t* SB, int fmt, const float* GS,
+                                   const int32_t* offsets, int E, int N, int K, uint16_t* C, int grid,
+                                   hipStream_t stream);
 hipError_t launch_quant_gather(const uint16_t* x, int T, int K, const int32_t* row_of_slot, int top_k, int R,
                                uint8_t* A, float* SA, int layout, hipStream_t stream);
 

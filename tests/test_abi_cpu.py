@@ -206,6 +206,26 @@ def test_grouped_gemm_swiglu_host_validation(lib):
     assert lib.w4a8_last_error() != b""
 
 
+def test_grouped_gemm_a16_host_validation(lib):
+    f = lib.w4a8_grouped_gemm_a16
+    ok = (P16, P16, P16, 0, NUL, P16, 8, 256, 512, P16, NUL)
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=0) == 2                       # E = 0
+    assert call(a6=(1 << 16) + 1) == 2           # E past the limit
+    assert call(a7=40) == 2 and call(a7=0) == 2  # N % 16, N = 0
+    assert call(a8=500) == 2 and call(a8=0) == 2  # K % 128, K = 0
+    assert call(a3=2) == 3 and call(a3=-1) == 3  # unknown weight-scale format
+    assert call(a0=NUL) == 1 and call(a1=NUL) == 1 and call(a2=NUL) == 1 and call(a5=NUL) == 1 \
+        and call(a9=NUL) == 1
+    assert call(a0=P4) == 4 and call(a1=P4) == 4 and call(a9=P4) == 4 and call(a4=ctypes.c_void_p(0x1002)) == 4
+    assert lib.w4a8_last_error() != b""
+
+
 def test_binding_fails_loudly_without_gpu():
     import torch
     if torch.cuda.is_available():
