@@ -468,6 +468,42 @@ def measure_gemm_planned_wide_pool(reps=5, E=6144):
     return out
 
 
+def measure_gemm_a16(fmt, name="decode_gateup", reps=30):
+    """The grouped GEMM with bf16 activations and FP4 weights
+    (w4a8_grouped_gemm_a16) on a workload's shapes and routing: bf16 N(0,1)
+    activations, N(0, 0.02) weights quantized to MXFP4 (fmt 0) or NVFP4 (fmt
+    1, with a per-expert tensor scale), weights rotated past the Infinity
+    Cache.  HBM roofline on the bytes the launch must move."""
+    import torch
+
+    import moe_grouped_precision_amd as w4a8
+    import synth
+
+    p = synth.make_a16_problem(name, fmt, device="cuda")
+    counts, off, _ = w4a8.route_prep(p.topk_ids.to("cuda"), p.E)
+    counts = counts.cpu().numpy()
+    wbytes = p.B.numel() + p.SB.numel()
+    nrot = _rotations(wbytes)
+    Bs = [p.B] + [p.B.clone() for _ in range(nrot - 1)]
+    SBs = [p.SB] + [p.SB.clone() for _ in range(nrot - 1)]
+    GS = p.GS if fmt == 1 else None
+    C = torch.empty((p.R, p.N), dtype=torch.bfloat16, device="cuda")
+    ms = time_launches(lambda i: w4a8.grouped_gemm_a16(p.A, Bs[i % nrot], SBs[i % nrot], fmt, off, GS, out=C),
+                       reps, warmup=10)
+    hit = int((counts > 0).sum())
+    blk = 32 if fmt == 0 else 16
+    nbytes = hit * p.N * p.K * (0.5 + 1.0 / blk) + p.R * p.K * 2 + p.R * p.N * 2 + 4 * (p.E + 1) + 4 * p.E * fmt
+    flops = 2.0 * p.R * p.N * p.K
+    cfg = p.name
+    out = _hbm_result(f"{cfg}: E={p.E} top_k={p.top_k} tokens={p.T} routed_rows={p.R} N={p.N} K={p.K}, bf16 "
+                      f"activations, {'MXFP4 (E8M0 per 32)' if fmt == 0 else 'NVFP4 (E4M3 per 16, fp32 per expert)'}"
+                      f" weights", ms, nbytes, flop=flops,
+                      tflops=round(flops / (statistics.median(ms) * 1e-3) / 1e12, 1), weight_copies_rotated=nrot)
+    del Bs, SBs, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_gemm_swiglu(reps=10):
     """The gate/up GEMM with the SwiGLU + E4M3 requantization epilogue
     (w4a8_grouped_gemm_swiglu) on the large prefill gate/up workload (16384
@@ -653,9 +689,12 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        log("timing the fused gate/up + SwiGLU GEMM, the activation quantizer, SwiGLU requantization, "
+        log("timing the fused gate/up + SwiGLU GEMM, the A16 GEMMs, the activation quantizer, SwiGLU requantization, "
             "the top-k combine, the routing prep over 6144 experts and the GEMM over 2048 experts")
         extras = {"grouped_gemm_swiglu": measure_gemm_swiglu(),
+                  "grouped_gemm_a16_mxfp4": measure_gemm_a16(0), "grouped_gemm_a16_nvfp4": measure_gemm_a16(1),
+                  "grouped_gemm_a16_mxfp4_e12_w2_m8": measure_gemm_a16(0, "e12_w2_m8"),
+                  "grouped_gemm_a16_nvfp4_e12_w2_m8": measure_gemm_a16(1, "e12_w2_m8"),
                   "quantize_gather": measure_quantize_gather(), "swiglu_quant": measure_swiglu_quant(),
                   "combine": measure_combine(), "route_prep_wide_pool": measure_route_prep_wide(),
                   "grouped_gemm_wide_pool": measure_gemm_wide_pool(),

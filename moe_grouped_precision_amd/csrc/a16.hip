@@ -18,11 +18,13 @@
 // name as what dominates the remaining NVFP4 gap (humming PR #58, "H200
 // performance", the BF16 FP4 expert-GEMM sweeps).
 //
-// Work: items (expert, 64 output columns) over a grid of workgroups of four
-// waves; wave w owns columns 16 w .. 16 w + 15 of the item and up to 64 of
-// the expert's rows at a time (further rows in further passes over K).  Per
-// 128-K group a lane loads 16 bytes of weights (column l % 16, K 32 q .. 32 q
-// + 31, q = l / 16), converts them, and the group's 8 MFMAs per row block
+// Work: items (expert, 128 output columns) over a grid of workgroups of four
+// waves; wave w owns columns 32 w .. 32 w + 31 of the item (two blocks of 16)
+// and up to 64 of the expert's rows at a time (further rows in further
+// passes over K, one code path per number of row blocks).  Per 128-K group
+// and column block a lane loads 16 bytes of weights (column l % 16 of the
+// block, K 32 q .. 32 q + 31, q = l / 16; two groups ahead), converts them,
+// and the group's 8 MFMAs per row and column block
 // take K in the order k = 32 q + 4 j + t (MFMA j, lane group q, element t):
 // a lane's own 32 weights feed its 8 MFMAs, and the activation fragments
 // follow the same order from LDS.  Activation rows are staged in LDS, two
@@ -43,7 +45,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int A16_THREADS = 256;
-constexpr int A16_COLS = 64;                 // output columns per item
+constexpr int A16_COLS = 128;                // output columns per item (32 per wave)
 constexpr int A16_ROWS = 64;                 // rows per pass
 constexpr int A16_ROW_BYTES = 256;           // 128 bf16 of one row per K group
 constexpr int A16_BUF = A16_ROWS * A16_ROW_BYTES;   // 16 KB per buffer
@@ -93,6 +95,134 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
   return __builtin_bit_cast(float, c << 23);
 }
 
+// One pass over K for rows r0 .. r0 + rows - 1 (NRB = ceil(rows / 16) row
+// blocks) of expert e and the lane's two weight columns: activations staged
+// in LDS one group ahead, weights and their scale codes loaded two groups
+// ahead in registers.
+template <int FMT, int NRB>
+__device__ __forceinline__ void a16_pass(const uint16_t* __restrict__ A, const uint8_t* const (&wcol)[2],
+                                         const uint8_t* const (&scol)[2], const bool (&wvalid)[2], float gs,
+                                         int r0, int rows, int K, int N, int col0, uint8_t* lds,
+                                         uint16_t* __restrict__ C) {
+  constexpr int SPG = FMT == 0 ? 4 : 8;       // scale codes per column per K group
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int G = K >> 7;
+  // activation staging: the pass's row blocks x 16 chunks of 16 bytes per
+  // group, NRB per thread (rows past `rows` inside the last block re-read
+  // the last row)
+  auto load_act = [&](int g, v4u (&ra)[NRB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int ch = threadIdx.x + i * A16_THREADS;
+      const int rr = min(ch >> 4, rows - 1);
+      ra[i] = *reinterpret_cast<const v4u*>(A + (size_t)(r0 + rr) * K + (size_t)g * 128 + (ch & 15) * 8);
+    }
+  };
+  auto store_act = [&](int buf, const v4u (&ra)[NRB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int ch = threadIdx.x + i * A16_THREADS;
+      const int rr = ch >> 4;
+      *reinterpret_cast<v4u*>(lds + buf * A16_BUF + rr * A16_ROW_BYTES + (((ch & 15) ^ (rr & 15)) << 4)) = ra[i];
+    }
+  };
+  auto load_w = [&](int g, v4u (&w)[2], uint32_t (&sc)[2]) __attribute__((always_inline)) {
+    const int gc = min(g, G - 1);   // past the last group: re-read it (never used)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      w[cb] = *reinterpret_cast<const v4u*>(wcol[cb] + (size_t)gc * 64);
+      if (FMT == 0)
+        sc[cb] = scol[cb][gc * SPG + q];
+      else
+        sc[cb] = *reinterpret_cast<const uint16_t*>(scol[cb] + gc * SPG + 2 * q);
+    }
+  };
+
+  v4f acc[NRB][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4u ra[NRB], w0[2], w1[2];
+  uint32_t s0c[2], s1c[2];
+  load_act(0, ra);
+  load_w(0, w0, s0c);
+  load_w(1, w1, s1c);
+  store_act(0, ra);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    if (g + 1 < G) load_act(g + 1, ra);
+    v4u w2[2];
+    uint32_t s2c[2];
+    load_w(g + 2, w2, s2c);
+    // this group's weights as bf16 MFMA operands: wb[cb][2j], wb[cb][2j+1] = k 32q + 4j .. +3
+    uint32_t wb[2][16];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float sa = FMT == 0 ? e8m0_to_f32(s0c[cb]) : e4m3_to_f32(s0c[cb] & 0xFF);
+      const float sb = FMT == 0 ? sa : e4m3_to_f32(s0c[cb] >> 8);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t t[4];
+        e2m1x8_to_bf16(w0[cb][d], d < 2 ? sa : sb, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wb[cb][4 * d + i] = t[i];
+      }
+    }
+    const uint8_t* ab = lds + buf * A16_BUF;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = rb * 16 + c16;
+      const uint8_t* arow = ab + r * A16_ROW_BYTES;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // MFMAs 2 jj and 2 jj + 1 read bytes 64 q + 16 jj .. +15 of the row (chunk 4 q + jj)
+        const v4u x = *reinterpret_cast<const v4u*>(arow + (((4 * q + jj) ^ (r & 15)) << 4));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = 2 * jj + h;
+          const v4s b = __builtin_bit_cast(v4s, v2u{x[2 * h], x[2 * h + 1]});
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            const v4s a = __builtin_bit_cast(v4s, v2u{wb[cb][2 * j], wb[cb][2 * j + 1]});
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc[rb][cb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (g + 1 < G) store_act(buf ^ 1, ra);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      w0[cb] = w1[cb];
+      s0c[cb] = s1c[cb];
+      w1[cb] = w2[cb];
+      s1c[cb] = s2c[cb];
+    }
+    __syncthreads();
+  }
+  // D[n][m] of each (row block, column block): lane holds columns 4q .. 4q+3
+  // of the block for row c16 of the row block
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int m = rb * 16 + c16;
+    if (m < rows) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        if (wvalid[cb]) {
+          const v4f o = acc[rb][cb] * gs;
+          v2u pk;
+          pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){o[0], o[1]}, v2bf));
+          pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){o[2], o[3]}, v2bf));
+          *reinterpret_cast<v2u*>(C + (size_t)(r0 + m) * N + col0 + wave * 32 + cb * 16 + 4 * q) = pk;
+        }
+      }
+    }
+  }
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(A16_THREADS)
 grouped_gemm_a16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -109,124 +239,33 @@ grouped_gemm_a16_kernel(const uint16_t* __restrict__ A, const uint8_t* __restric
   if (s_bad) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane >> 4, c16 = lane & 15;
-  const int G = K >> 7;
+  const int c16 = lane & 15, q = lane >> 4;
   const int NB = (N + A16_COLS - 1) / A16_COLS;
   const int items = E * NB;
-  constexpr int SPG = FMT == 0 ? 4 : 8;       // scale codes per column per K group
-
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int e = it / NB, nb = it - e * NB;
     const int lo = offsets[e], hi = offsets[e + 1];
-    const int n = nb * A16_COLS + wave * 16 + c16;     // this lane's weight column
-    const bool wvalid = nb * A16_COLS + wave * 16 < N;  // N % 16 == 0: a wave's columns are all in or all out
-    const int ncl = min(n, N - 1);
-    const uint8_t* wcol = B + ((size_t)e * N + ncl) * (size_t)(K >> 1) + q * 16;
-    const uint8_t* scol = SB + ((size_t)e * N + ncl) * (size_t)(FMT == 0 ? K >> 5 : K >> 4);
+    // this lane's two weight columns (blocks cb = 0, 1 of the wave's 32);
+    // N % 16 == 0, so a block's 16 columns are all in or all out
+    const uint8_t* wcol[2];
+    const uint8_t* scol[2];
+    bool wvalid[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int nblk = nb * A16_COLS + wave * 32 + cb * 16;
+      wvalid[cb] = nblk < N;
+      const int ncl = min(nblk + c16, N - 1);
+      wcol[cb] = B + ((size_t)e * N + ncl) * (size_t)(K >> 1) + q * 16;
+      scol[cb] = SB + ((size_t)e * N + ncl) * (size_t)(FMT == 0 ? K >> 5 : K >> 4);
+    }
     const float gs = GS ? GS[e] : 1.0f;
     for (int r0 = lo; r0 < hi; r0 += A16_ROWS) {
       const int rows = min(A16_ROWS, hi - r0);
-      const int nrb = (rows + 15) >> 4;
-      // activation staging: 64 rows x 16 chunks of 16 bytes per group, four per thread
-      auto load_act = [&](int g, v4u (&ra)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = threadIdx.x + i * A16_THREADS;
-          const int rr = min(ch >> 4, rows - 1);
-          ra[i] = *reinterpret_cast<const v4u*>(A + (size_t)(r0 + rr) * K + (size_t)g * 128 + (ch & 15) * 8);
-        }
-      };
-      auto store_act = [&](int buf, const v4u (&ra)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = threadIdx.x + i * A16_THREADS;
-          const int rr = ch >> 4;
-          *reinterpret_cast<v4u*>(lds + buf * A16_BUF + rr * A16_ROW_BYTES + (((ch & 15) ^ (rr & 15)) << 4)) = ra[i];
-        }
-      };
-      auto load_w = [&](int g, v4u& w, uint32_t& sc) __attribute__((always_inline)) {
-        w = *reinterpret_cast<const v4u*>(wcol + (size_t)g * 64);
-        if (FMT == 0)
-          sc = scol[g * SPG + q];
-        else
-          sc = *reinterpret_cast<const uint16_t*>(scol + g * SPG + 2 * q);
-      };
-
-      v4f acc[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-      v4u ra[4], w;
-      uint32_t sc;
-      load_act(0, ra);
-      load_w(0, w, sc);
-      store_act(0, ra);
-      __syncthreads();
-      for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        v4u wn = w;
-        uint32_t scn = sc;
-        if (g + 1 < G) {
-          load_act(g + 1, ra);
-          load_w(g + 1, wn, scn);
-        }
-        // this group's weights as bf16 MFMA operands: wb[j] = k 32q + 4j .. +3
-        uint32_t wb[16];
-        {
-          const float s0 = FMT == 0 ? e8m0_to_f32(sc) : e4m3_to_f32(sc & 0xFF);
-          const float s1 = FMT == 0 ? s0 : e4m3_to_f32(sc >> 8);
-          uint32_t t[4];
-          e2m1x8_to_bf16(w[0], s0, t);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wb[i] = t[i];
-          e2m1x8_to_bf16(w[1], s0, t);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wb[4 + i] = t[i];
-          e2m1x8_to_bf16(w[2], s1, t);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wb[8 + i] = t[i];
-          e2m1x8_to_bf16(w[3], s1, t);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wb[12 + i] = t[i];
-        }
-        const uint8_t* ab = lds + buf * A16_BUF;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          if (rb < nrb) {
-            const int r = rb * 16 + c16;
-            const uint8_t* arow = ab + r * A16_ROW_BYTES;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              // MFMAs 2 jj and 2 jj + 1 read bytes 64 q + 16 jj .. +15 of the row (chunk 4 q + jj)
-              const v4u x = *reinterpret_cast<const v4u*>(arow + (((4 * q + jj) ^ (r & 15)) << 4));
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const int j = 2 * jj + h;
-                const v4s a = __builtin_bit_cast(v4s, v2u{wb[2 * j], wb[2 * j + 1]});
-                const v4s b = __builtin_bit_cast(v4s, v2u{x[2 * h], x[2 * h + 1]});
-                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc[rb], 0, 0, 0);
-              }
-            }
-          }
-        }
-        if (g + 1 < G) store_act(buf ^ 1, ra);
-        w = wn;
-        sc = scn;
-        __syncthreads();
-      }
-      // D[n][m] of each row block: lane holds columns 4q .. 4q+3 of the wave's
-      // 16 for row c16 of the block
-      if (wvalid) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int m = rb * 16 + c16;
-          if (rb < nrb && m < rows) {
-            const v4f o = acc[rb] * gs;
-            v2u p;
-            p[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){o[0], o[1]}, v2bf));
-            p[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){o[2], o[3]}, v2bf));
-            *reinterpret_cast<v2u*>(C + (size_t)(r0 + m) * N + nb * A16_COLS + wave * 16 + 4 * q) = p;
-          }
-        }
+      switch ((rows + 15) >> 4) {
+        case 1: a16_pass<FMT, 1>(A, wcol, scol, wvalid, gs, r0, rows, K, N, nb * A16_COLS, lds, C); break;
+        case 2: a16_pass<FMT, 2>(A, wcol, scol, wvalid, gs, r0, rows, K, N, nb * A16_COLS, lds, C); break;
+        case 3: a16_pass<FMT, 3>(A, wcol, scol, wvalid, gs, r0, rows, K, N, nb * A16_COLS, lds, C); break;
+        default: a16_pass<FMT, 4>(A, wcol, scol, wvalid, gs, r0, rows, K, N, nb * A16_COLS, lds, C); break;
       }
     }
   }
