@@ -349,26 +349,61 @@ struct MfmaTile {
     if constexpr (FUSED) {
       fused_epilogue(acc);
     } else if (wvalid) {
-      // lane coordinates recomputed (opaque) rather than kept live through the K loop
-      int t = threadIdx.x;
-      asm volatile("" : "+v"(t));
-      const int eq = (t >> 4) & 3, er = t & 15;
-      const int ncol = n0 + (t >> 6) * 64 + eq * 4;
-      const int N = p.N;
+      plain_epilogue(acc);
+    }
+    return nt;
+  }
+
+  // bf16 epilogue.  A lane holds 4 consecutive columns (8 bytes) of one row
+  // per accumulator block; stored as they are, a store instruction writes 32-
+  // byte pieces of 16 rows, and the tile's stores touch four times as many
+  // cache lines as it has, all workgroups at once.  So each wave passes its
+  // 64 columns through 4 KB of its own in ring slots 4-5 (free: the next
+  // tile's first loads fill slots 0-3 and scale chunk 0, and slots 4-5 are
+  // refilled only after that tile's first barrier, which every wave reaches
+  // after this), two row blocks at a time, and stores whole rows: 128 bytes
+  // (8 lanes x 16) per row.  In the staging rows 16-byte chunk c of row r is
+  // at c ^ (r & 7).
+  __device__ __forceinline__ void plain_epilogue(v4f (&acc)[8][4]) {
+    // lane coordinates recomputed (opaque) rather than kept live through the K loop
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int w = t >> 6, l = t & 63;
+    const int eq = (t >> 4) & 3, er = t & 15;
+    const int N = p.N;
+    uint8_t* st = lds + 4 * P2_XSLOT + w * 4096;
+    const int lr = l >> 3, lc = l & 7;              // read: row lr (+8u), chunk lc
+    const int col = n0 + w * 64 + lc * 8;           // first of the chunk's 8 columns
 #pragma unroll
-      for (int mi = 0; mi < NMB; ++mi) {
-        const int m = mi * 16 + er;
-        if (m < rows) {
-          uint16_t* crow = p.C + (size_t)(row0 + m) * N;
+    for (int rb = 0; rb < (NMB + 1) / 2; ++rb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int mi = 2 * rb + h;
+        if (mi < NMB) {
+          const int r = h * 16 + er;
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
-            const int n = ncol + nb * 16;
-            if (n < N) store_bf16x4(crow + n, acc[mi][nb]);
+            const int c = 2 * nb + (eq >> 1);
+            const v4f v = acc[mi][nb];
+            const v2bf lo = __builtin_convertvector((v2f){v[0], v[1]}, v2bf);
+            const v2bf hi = __builtin_convertvector((v2f){v[2], v[3]}, v2bf);
+            uint2 o;
+            o.x = __builtin_bit_cast(uint32_t, lo);
+            o.y = __builtin_bit_cast(uint32_t, hi);
+            *reinterpret_cast<uint2*>(st + r * 128 + ((c ^ (r & 7)) << 4) + (eq & 1) * 8) = o;
           }
         }
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = u * 8 + lr;               // staging row
+        const int m = rb * 32 + r;              // tile row
+        if (m < rows && (2 * rb + (r >> 4)) < NMB) {
+          const v4i v = *reinterpret_cast<const v4i*>(st + r * 128 + ((lc ^ (r & 7)) << 4));
+          if (col < N) *reinterpret_cast<v4i*>(p.C + (size_t)(row0 + m) * N + col) = v;
+        }
+      }
     }
-    return nt;
   }
 
   // Fused SwiGLU epilogue: lane (q, i) holds, for row block mi, gate in
