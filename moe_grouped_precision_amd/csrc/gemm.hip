@@ -41,38 +41,64 @@ grouped_gemm_kernel(GemmArgs p) {
   __shared__ int s_eord[MAX_EXPERTS];
   __shared__ int s_rrc[5][4];
   constexpr int smax = FUSED ? 0 : S_MAX;
-  if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info, smax)) return;
-  const int R = uniform(s_off[p.E]);
+  bool have_plan = false;
 
-  // phase 1: streaming items
+  // phase 1: streaming items.  The workgroup's items come either from one
+  // block range of one expert (split into ceil(range / cap) items) or from
+  // the round-robin dealing; one call site runs them all, so each item shape
+  // is compiled once.
   if constexpr (!FUSED) {
-    const int tiles = uniform(s_sbase[p.E]);
-    const int nu = (p.N + 63) / 64;
-    if (tiles > 0 && uniform(s_info[1]) == uniform(s_info[2]) &&
-        (long long)tiles * nu >= 2LL * gridDim.x) {
-      // every streaming tile has the same row blocks, so every 64-column unit
-      // costs the same: an equal share of units per workgroup (with fewer
-      // than two units per workgroup, dealing whole items measured faster)
-      long long u = 0, u_end = 0;
-      stream_range(tiles, nu, blockIdx.x, gridDim.x, &u, &u_end);
-      while (u < u_end) {
-        const int mt = (int)(u / nu);
-        const int c0 = (int)(u - (long long)mt * nu);
-        const int w = (int)min((long long)min(P1_RANGE_MAXNBW, nu - c0), u_end - u);
-        const int e = uniform(expert_of_tile(s_sbase, p.E, mt));
-        const int row0 = uniform(s_off[e]);
-        const int rows = uniform(s_off[e + 1]) - row0;
-        stream_item(p, lds, e, row0, rows, c0 * 64, w, R);
-        u += w;
+    int mode = 0;                          // 1: block range, 2: round robin
+    bool need_mfma = true;
+    int e = 0, row0 = 0, rows = 0, b0 = 0, b1 = 0, R = 0, items = 0;
+    if (p.E < 64 && (int)gridDim.x >= 64 && (int)gridDim.x < 4096) {
+      // small pools: every wave finds the workgroup's expert and blocks in
+      // registers; the plan tables of the MFMA phase are built afterwards
+      const StreamAssign a = stream_assign_small(p.offsets, p.E, p.N >> 4, blockIdx.x, gridDim.x);
+      if (!a.valid) return;
+      if (a.tiles > 0) {
+        mode = 1;
+        e = uniform(a.e); row0 = uniform(a.row0); rows = uniform(a.rows);
+        b0 = uniform(a.b0); b1 = uniform(a.b1); R = uniform(a.R);
       }
-    } else if (tiles > 0) {
-      // tiles of different row blocks: items dealt round-robin in a snake
-      // order of decreasing cost, each expert's items as wide as its row
-      // blocks allow up to the cap the plan picks
-      stream_rr_plan(s_off, p.E, nu, gridDim.x, s_eord, s_rrc);
-      const int items = uniform(s_rrc[4][0]);
-      const int G = gridDim.x;
-      for (int r = 0;; ++r) {
+      need_mfma = a.any_mfma;
+    } else {
+      if (!plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info, smax)) return;
+      have_plan = true;
+      need_mfma = uniform(s_mbase[p.E]) > 0;
+      R = uniform(s_off[p.E]);
+      const int tiles = uniform(s_sbase[p.E]);
+      if (tiles > 0 && tiles <= (int)gridDim.x && (int)gridDim.x < ST_EXP) {
+        // one expert per workgroup: its share of that expert's 16-column
+        // blocks, as few items as the register budget allows
+        stream_alloc(s_off, s_sbase, p.E, gridDim.x, s_eord);
+        stream_expert_range(s_eord, tiles, p.N >> 4, blockIdx.x, gridDim.x, &e, &b0, &b1);
+        row0 = uniform(s_off[e]);
+        rows = uniform(s_off[e + 1]) - row0;
+        mode = 1;
+      } else if (tiles > 0) {
+        // more experts than workgroups: items of 128-column units dealt
+        // round-robin in a snake order of decreasing cost, each expert's
+        // items as wide as its row blocks allow up to the cap the plan picks
+        stream_rr_plan(s_off, p.E, (p.N + 127) / 128, gridDim.x, s_eord, s_rrc);
+        items = uniform(s_rrc[4][0]);
+        mode = 2;
+      }
+    }
+    // block range: ceil(range / cap) items of nearly equal width (cap 32
+    // blocks, 24 with four row blocks)
+    static_assert(stream_max_nbw(3) == 4 && stream_max_nbw(4) == 3, "items of 32 or 24 blocks");
+    const uint32_t n = (uint32_t)(b1 - b0);
+    const uint32_t ni = mode != 1 ? 0 : (rows + 15) >> 4 <= 3 ? (n + 31) >> 5 : (n + 23) / 24;
+    const int G = gridDim.x;
+    for (int r = 0; mode != 0; ++r) {
+      int n0, nb;
+      if (mode == 1) {
+        if ((uint32_t)r >= ni) break;
+        const int c0 = b0 + (int)(n * r / ni), c1 = b0 + (int)(n * (r + 1) / ni);
+        n0 = c0 * 16;
+        nb = c1 - c0;
+      } else {
         const int it = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
         if (it >= items) break;  // item numbers never decrease from one round to the next
         int k = 0;
@@ -80,14 +106,19 @@ grouped_gemm_kernel(GemmArgs p) {
         const int rel = it - uniform(s_rrc[k][0]);
         const int ipe = uniform(s_rrc[k][2]), w = uniform(s_rrc[k][3]);
         const int q = rel / ipe;
-        const int e = uniform(s_eord[uniform(s_rrc[k][1]) + q]);
-        const int row0 = uniform(s_off[e]);
-        const int rows = uniform(s_off[e + 1]) - row0;
+        e = uniform(s_eord[uniform(s_rrc[k][1]) + q]);
+        row0 = uniform(s_off[e]);
+        rows = uniform(s_off[e + 1]) - row0;
         const int c0 = (rel - q * ipe) * w;
-        stream_item(p, lds, e, row0, rows, c0 * 64, min(w, nu - c0), R);
+        n0 = c0 * 128;
+        nb = min(8 * w, (p.N >> 4) - 8 * c0);
       }
+      stream_item(p, lds, uniform(e), uniform(row0), uniform(rows), uniform(n0), uniform(nb), uniform(R));
     }
+    if (!need_mfma) return;
   }
+  if (!have_plan && !plan_prologue(p.offsets, p.E, s_off, s_sbase, s_mbase, s_info, smax)) return;
+  const int R = uniform(s_off[p.E]);
 
   // phase 2: MFMA tiles, one workgroup each; each tile issues the first
   // shared-operand loads of the workgroup's next tile before its epilogue
@@ -154,12 +185,11 @@ grouped_gemm_planned_kernel(GemmArgs p) {
   const int nm = max(0, min(uniform(p.plan[3]), p.max_tiles - ns));
   const int G = gridDim.x;
 
-  // phase 1: streaming tiles, items of (up to) three 64-column units dealt
-  // round-robin in a snake order
+  // phase 1: streaming tiles, items of up to P1_MAXNB blocks of 16 columns
+  // dealt round-robin in a snake order
   {
-    const int nu = (p.N + 63) / 64;
-    constexpr int W = P1_RANGE_MAXNBW;
-    const int ipt = (nu + W - 1) / W;
+    const int NB = p.N >> 4;
+    const int ipt = (NB + P1_MAXNB - 1) / P1_MAXNB;
     const long long items = (long long)ns * ipt;
     for (long long r = 0;; ++r) {
       const long long it = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
@@ -167,7 +197,14 @@ grouped_gemm_planned_kernel(GemmArgs p) {
       const int t = (int)(it / ipt), c = (int)(it - (long long)t * ipt);
       int e, row0, rows;
       if (!planned_tile(p, R, t, CLASS_STREAM, S_MAX, &e, &row0, &rows)) continue;
-      stream_item(p, lds, e, row0, rows, c * W * 64, min(W, nu - c * W), R);
+      // as one or two items, as the tile's row blocks allow
+      const int b0 = c * P1_MAXNB, nb = min(P1_MAXNB, NB - b0);
+      const int cap = 8 * stream_max_nbw((rows + 15) >> 4);
+      const int ni = (nb + cap - 1) / cap;
+      for (int k = 0; k < ni; ++k) {
+        const int c0 = b0 + nb * k / ni, c1 = b0 + nb * (k + 1) / ni;
+        stream_item(p, lds, e, row0, rows, c0 * 16, c1 - c0, R);
+      }
     }
   }
 

@@ -2,149 +2,175 @@
 // experts with at most S_MAX rows (decode-sized batches, where HBM bandwidth
 // is the limit).  gfx950 only.
 //
-// One workgroup of 512 threads (8 waves) per item (expert, 64..192 columns,
-// width picked per launch): waves 0-3 take the first half of the K groups
-// and waves 4-7 the second half, two groups per stage.  Weights stream from
-// HBM straight into MFMA operand registers (a per-wave ring two stages deep);
-// the activation rows and the scales are shared through LDS with direct
-// global->LDS loads (global_load_lds_dwordx4 / _dword), which hold no
-// registers while in flight: every wave issues the same number of loads per
-// stage, waits for the stage it needs with one explicit vmcnt and meets the
-// others at one barrier per stage.  The halves are added in LDS (always half
-// 0 + half 1) before the bf16 store.  The E8M0 and activation scales are
-// loaded four groups at a time (four lanes read 16 contiguous bytes) into a
-// double buffer.  The XOR swizzle that keeps fragment reads free of LDS bank
-// conflicts is applied on the global-address side (a load lane always writes
-// slot base + size * lane).  All loads use clamped addresses (padding rows and
-// columns re-read a real one and are never stored), so no load is
-// conditional on data.
+// An item is (expert, nb blocks of 16 weight columns, the whole K).  Its 8
+// waves own distinct blocks (block 8j + w is wave w's j-th, so every wave has
+// at most one block more than another) and each wave walks the whole K for
+// them: no partial sums are exchanged, the accumulators go straight to bf16.
+// Weights stream from HBM straight into MFMA operand registers through a
+// per-wave ring of D stages (no LDS: no other wave needs them); the
+// activation rows and the scales are shared by the workgroup and come
+// through LDS with direct global->LDS loads (global_load_lds_dwordx4 /
+// _dword), which hold no registers while in flight.  Every wave issues the
+// same number of ring loads per stage (blocks past the item's end load with
+// exec = 0), waits for the stage it needs with one explicit vmcnt and meets
+// the others at one barrier per stage.  The depth D grows as the item
+// narrows, so a workgroup keeps about the same weight bytes in flight
+// (8 waves x D stages x NBW blocks x 2 KB: 64-144 KB) whatever its width.
+// The XOR swizzle that keeps fragment reads free of LDS bank conflicts is
+// applied on the global-address side (a load lane always writes slot base +
+// size * lane).  All loads use clamped addresses (padding rows and columns
+// re-read a real one and are never stored), so no load is conditional on
+// data.
 #pragma once
 
 #include "w4a8_kernel.h"
 
 namespace w4a8 {
 
-// ---------------------------------------------------------------------------
-// Phase 1: weight streaming (experts with <= S_MAX rows)
-//
-// A workgroup item is (expert, 64*NBW columns).  Waves 0-3 take the first half
-// of the K groups, waves 4-7 the second half; a stage is KG consecutive groups
-// of each half; wave w owns NBW 16-column blocks.  Weights go straight from
-// HBM into the MFMA operand registers through a per-wave ring of D stages (no
-// LDS: no other wave needs them); the activation rows and both scale kinds
-// are shared by the workgroup and come through LDS:
-//   X ring   : D+1 slots x [KG][2 halves][64 rows][128 B] @ 0  (row chunk c at c ^ (row & 7))
-//   SB chunk : 2 x [2 halves][64*NBW cols][SC] u32            @ P1_SB
-//   SA chunk : 2 x [2 halves][64 rows][SC] fp32               @ P1_SB + 2 * SBS
-// Stage s: wait (the weights of stage s and, older, its activation rows have
-// landed), barrier, issue the activation rows of stage s + D, MFMAs, then the
-// weights of stage s + D into the register slot just used.  After the K loop
-// the halves are added through LDS (always half 0 + half 1, whatever the item
-// width or stage size), then rounded to bf16 and stored.
-// ---------------------------------------------------------------------------
-constexpr int P1_XGROUP = 16384;          // activation rows of one group, both halves
-constexpr int P1_XRING = 6 * P1_XGROUP;   // (D+1)*KG groups, at most 96 KB
-// widest item in 64-column units, per row blocks of the expert (the weight
-// ring, 16*NBW registers, and the accumulators, 4*NBW*MB, share the
-// register file with the MFMA operands)
-constexpr int P1_MAXNBW = 4;
-__host__ __device__ constexpr int stream_max_nbw(int mb) { return mb <= 2 ? 4 : 3; }
-// items of a contiguous range are at most this wide (wider measured no faster)
-constexpr int P1_RANGE_MAXNBW = 3;
-// groups of K per streaming stage: two halve the per-stage barriers and LDS
-// round trips against one, at the same bytes in flight (four, with a single
-// stage in flight, measured slower)
+// groups of K per stage: a stage's weight loads cover one whole 128-byte
+// line (two groups) per column, paired into the two groups' operands by DPP
 constexpr int P1_KG = 2;
-constexpr int P1_SB = P1_XRING;
-// SB chunk buffers are max(6 KB, NBW * 2 KB) apart: items up to three units
-// wide keep the 6 KB spacing (an 8 KB spacing measured 5% slower for them)
-__host__ __device__ constexpr int stream_sb_stride(int nbw) { return nbw <= 3 ? 6144 : 2048 * nbw; }
-constexpr int P1_SBMAX = 2 * stream_sb_stride(P1_MAXNBW);
-constexpr int P1_SABUF = 2 * 64 * SC * 4;                  // 2 KB
-constexpr int P1_BYTES = P1_SB + P1_SBMAX + 2 * P1_SABUF;
+// blocks per wave: the accumulators (4 * NBW * MB), the weight ring
+// (8 * D * NBW) and the paired operands (8 * NBW) share the register file
+constexpr int P1_MAXNBW = 4;
+__host__ __device__ constexpr int stream_max_nbw(int mb) { return mb <= 3 ? 4 : 3; }
+// stages in flight: about 8 block-stages of weights per wave with the whole
+// K per wave; two with the K split (where the LDS holds both parts' rows)
+__host__ __device__ constexpr int stream_depth(int nbw, int ks) { return ks == 2 ? 2 : (nbw <= 2 ? 4 : (nbw == 3 ? 3 : 2)); }
+// scale chunks (SC groups each) in LDS at once: a chunk is loaded D stages
+// ahead of its first use, while up to D * P1_KG / SC earlier chunks are live
+__host__ __device__ constexpr int stream_nbuf(int nbw, int ks) {
+  return (stream_depth(nbw, ks) * P1_KG + SC - 1) / SC + 1;
+}
+// activation ring slot: P1_KG groups x ks parts x 64 rows x 128 B; E8M0
+// chunk: 8 * nbw blocks x 16 columns x SC words; activation-scale chunk:
+// ks parts x 64 rows x SC words
+__host__ __device__ constexpr int stream_lds_bytes(int nbw, int ks) {
+  return (stream_depth(nbw, ks) + 1) * P1_KG * ks * 8192 +
+         stream_nbuf(nbw, ks) * (128 * nbw * SC * 4 + ks * 64 * SC * 4);
+}
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int P1_BYTES = cmax(cmax(cmax(stream_lds_bytes(3, 1), stream_lds_bytes(4, 1)),
+                                   cmax(stream_lds_bytes(1, 2), stream_lds_bytes(2, 2))),
+                              cmax(stream_lds_bytes(3, 2), stream_lds_bytes(4, 2)));
+// an item holds at most this many 16-column blocks
+constexpr int P1_MAXNB = 8 * P1_MAXNBW;
 
-template <int NBW, int KG, int MB>
+// An item of the streaming phase.  KS = 1: the 8 waves own distinct blocks
+// (block 8j + w is wave w's j-th) and walk the whole K.  KS = 2 (narrow
+// items, at most 16 blocks): waves 0-3 take the first ceil(G/2) groups of K
+// and waves 4-7 the rest, each half owning all the item's blocks (block 4j +
+// (w & 3)), so a narrow item runs half as many stages with twice the blocks
+// per wave; the halves are added in LDS (always half 0 + half 1) before the
+// bf16 store.
+template <int NBW, int MB, int KS>
 struct StreamItem {
-  static constexpr int WIDTH = 64 * NBW;  // columns per item
-  // stages in flight: KG*D groups of weights per wave
-  static constexpr int D = KG == 2 ? 2 : (NBW <= 2 ? 4 : 3);
-  static constexpr int NX = D + 1;        // activation ring slots
-  static constexpr int XSLOT = KG * P1_XGROUP;
-  static constexpr int PER = KG * (NBW + MB);  // ring loads per wave per stage
-  static_assert(NX * XSLOT <= P1_XRING, "activation ring");
+  static constexpr int KG = P1_KG;
+  static constexpr int WPK = 8 / KS;                 // waves per K part
+  static constexpr int D = stream_depth(NBW, KS);
+  static constexpr int NX = D + 1;                   // activation ring slots
+  static constexpr int NBUF = stream_nbuf(NBW, KS);  // scale chunk buffers
+  static constexpr int WIDTH = 16 * WPK * NBW;       // columns per item, at most
+  static constexpr int XSLOT = KG * KS * 8192;       // [group][part][64 rows][128 B]
+  static constexpr int SBB = KS * WIDTH * SC * 4;    // E8M0 words of a chunk: [part][column][group]
+  static constexpr int SAB = KS * 64 * SC * 4;       // activation scales of a chunk: [part][row][group]
+  static constexpr int SB0 = NX * XSLOT;
+  static constexpr int SA0 = SB0 + NBUF * SBB;
+  static constexpr int NXL = KS * MB;                // activation loads per wave per stage
+  static constexpr int PER = 2 * NBW + NXL;          // ring loads per wave per stage
+  static_assert(KS == 1 || KS == 2, "K parts");
+  static_assert(SA0 + NBUF * SAB <= P1_BYTES, "LDS layout");
   static_assert((D - 1) * PER < 64, "vmcnt range");
-  // a scale chunk buffer is reloaded D stages before the first stage of the
-  // chunk after next: every stage of the chunk before must be done by then
-  static_assert(SC % KG == 0 && D * KG <= SC, "scale chunk reuse distance");
-  static_assert(KG == 2, "a stage's weight loads cover one 128-byte line (two groups) per column");
+  static_assert(SC % KG == 0 && (NBUF - 1) * SC >= D * KG, "scale chunk reuse distance");
   static_assert(NBW <= stream_max_nbw(MB), "register budget");
-  static constexpr int SBS = stream_sb_stride(NBW);  // SB chunk buffer spacing
-  static constexpr int SAB = P1_SB + 2 * SBS;        // SA chunk buffers
-  static_assert(SBS >= 2 * 64 * NBW * SC * 4 && SAB + 2 * P1_SABUF <= P1_BYTES, "scale chunk buffers");
-  static_assert(4 * NBW * MB * 1024 <= P1_SB, "reduction scratch must fit below the scale chunks");
+  static_assert(SBB == KS * WIDTH * SC * 4 && KS * WIDTH <= 512, "one 16-byte E8M0 load per column covers a chunk");
+  static_assert(SBB == 8 * NBW * 256, "NBW 4-byte E8M0 loads per wave cover a chunk");
+  static_assert(4 * NBW * MB * 1024 * (KS - 1) <= SB0, "reduction scratch fits in the activation ring");
 
-  // Activation rows of stage s: 8*MB loads of 4 rows x 128 B per group, MB per
-  // wave (half a wave each).  xt = the item's first row.
-  __device__ __forceinline__ static void issue_x(const uint8_t* xt, const uint32_t (&xo)[MB], uint8_t* slot,
-                                                 int G, int s, bool live) {
-    const int wave = uniform(threadIdx.x >> 6);
-    const int Gh = (G + 1) / 2;
+  // Activation rows of stage s: KG groups x KS parts x 16*MB rows x 128 B in
+  // 8*NXL half-wave loads of 4 rows, NXL per wave.  xt = the item's first
+  // row; xo = this lane's row offsets; xg / xs = each load's group (from the
+  // part's first) and LDS offset; gbeg = the first group of each part.
+  __device__ __forceinline__ static void issue_x(const uint8_t* xt, const uint32_t (&xo)[NXL], const int (&xg)[NXL],
+                                                 const int (&xs)[NXL], uint8_t* slot, int G, int s, bool live) {
     const uint64_t mask = live_mask(live) & 0xffffffffull;  // lanes 0-31 load
 #pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      const int g0 = min(s * KG + kg, G - 1), g1 = min(Gh + s * KG + kg, G - 1);
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int jx = wave * MB + i;
-        const int h = jx / (4 * MB), quad = jx - h * (4 * MB);
-        vm_dma16(xt + (size_t)(h ? g1 : g0) * 128, xo[i],
-                 lds_u32(slot + kg * P1_XGROUP + h * 8192 + quad * 512), mask);
-      }
+    for (int i = 0; i < NXL; ++i) {
+      const int g = min(s * KG + xg[i], G - 1);
+      vm_dma16(xt + (size_t)g * 128, xo[i], lds_u32(slot + xs[i]), mask);
     }
   }
 
-  // Scale chunk c (groups SC*c .. SC*c+3 of each half): NBW SB + 1 SA loads per wave.
-  __device__ __forceinline__ static void issue_scales(const GemmArgs& p, uint8_t* lds, int e,
-                                                      int row0, int rows, int n0, int c, int R) {
+  // Scale chunk c (groups SC*c .. SC*c+SC-1 of each part) into buffer c % NBUF.
+  // E8M0: a column's codes of SC consecutive groups are 16 contiguous bytes,
+  // so one 16-byte load per column (lane idx = part * WIDTH + column; waves
+  // past the KS * WIDTH columns issue none; columns past the item's last
+  // real one re-read that one).  The load starts at chunk_start(c) clamped to
+  // G - SC so that it stays inside the column, and the word of group g then
+  // sits at g - load start (sb_shift).  With fewer than SC groups in all, one
+  // 4-byte load per (column, group) instead, the groups past the last clamped
+  // to it.  Activation scales: one 4-byte load per (part, row, group) on 4*KS
+  // waves.
+  __device__ __forceinline__ static void issue_scales(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows,
+                                                      int n0, int nlast, int gh, int c, int R) {
     const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
     const int K = p.K, N = p.N, G = K >> 7;
-    const int gb1 = (G + 1) / 2;
+    const int buf = c % NBUF;
+    if (G >= SC) {
+      if (wave * 64 < KS * WIDTH) {
+        const int idx = wave * 64 + lane;  // [part][col]
+        const int h = idx / WIDTH, col = idx - h * WIDTH;
+        const int n = min(n0 + col, nlast);
+        const int g = min(h * gh + SC * c, G - SC);
+        const uint32_t off = (uint32_t)(n - n0) * (uint32_t)(K >> 5) + (uint32_t)g * 4u;
+        vm_dma16(p.SB + ((size_t)e * N + n0) * (size_t)(K >> 5), off,
+                 lds_u32(lds + SB0 + buf * SBB + wave * 1024), live_mask(true));
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-      const int idx = (wave * NBW + i) * 64 + lane;  // [h][col][gg]
-      const int h = idx / (WIDTH * SC), rem = idx - h * (WIDTH * SC);
-      const int col = rem >> 2, gg = rem & 3;
-      const int n = min(n0 + col, N - 1);
-      const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
-      vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-              lds_u32(lds + P1_SB + (c & 1) * SBS + (wave * NBW + i) * 256));
+      for (int i = 0; i < NBW; ++i) {
+        const int idx = (wave * NBW + i) * 64 + lane;  // [part][col][gg]
+        const int h = idx / (WIDTH * SC), rem = idx - h * (WIDTH * SC);
+        const int col = rem >> 2, gg = rem & 3;
+        const int n = min(n0 + col, nlast);
+        const int g = min(h * gh + SC * c + gg, G - 1);
+        vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+                lds_u32(lds + SB0 + buf * SBB + (wave * NBW + i) * 256));
+      }
     }
-    {
-      const int idx = wave * 64 + lane;  // [h][row][gg]
+    if (wave < 4 * KS) {
+      const int idx = wave * 64 + lane;  // [part][row][gg]
       const int h = idx >> 8, r = (idx >> 2) & 63, gg = idx & 3;
       const size_t row = (size_t)row0 + min(r, rows - 1);
-      const int g = min((h ? gb1 : 0) + SC * c + gg, G - 1);
-      vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + SAB + (c & 1) * P1_SABUF + wave * 256));
+      const int g = min(h * gh + SC * c + gg, G - 1);
+      vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + SA0 + buf * SAB + wave * 256));
     }
+  }
+  // Word of the E8M0 chunk holding group gl (index within the part) of the
+  // part that starts at group gbase: gl % SC, plus the clamp of the load.
+  __device__ __forceinline__ static int sb_word(int gl, int gbase, int G) {
+    const int start = gbase + SC * (gl / SC);
+    return gl % SC + (G >= SC ? max(0, start - (G - SC)) : 0);
   }
 
   // Weights of this wave for the stage whose groups are gfirst, gfirst + 1:
-  // per 16-column block j, load w[h][j] covers columns 8h .. 8h+7 of the block
-  // with one full 128-byte line (both groups) per column, lane 16q + i reading
-  // column 8h + (i & 7), group gfirst + (i >> 3), bytes 16q .. 16q+15.  Whole
-  // lines per request stream from HBM at the rate of contiguous reads; two
-  // 64-byte requests per line (one per group) do not.  pair_operands() turns
-  // the two loads into the MFMA operands of the two groups.  wt = the item's
-  // first column; wo = this lane's column offsets; goff = its group offset
-  // (the second group is clamped to the last one when G is odd).
-  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt,
-                                                const uint32_t (&wo)[2][NBW], int gfirst, int G, bool live) {
+  // per block j, load w[h][j] covers columns 8h .. 8h+7 of the block with one
+  // full 128-byte line (both groups) per column, lane 16q + i reading column
+  // 8h + (i & 7), group gfirst + (i >> 3), bytes 16q .. 16q+15.  Whole lines
+  // per request stream from HBM at the rate of contiguous reads; two 64-byte
+  // requests per line (one per group) do not.  pair_operands() turns the two
+  // loads into the MFMA operands of the two groups.  wt = the item's first
+  // column; wo = this lane's column offsets; jmask[j] = exec of block j (0
+  // past the item's end); the second group is clamped to the last one when G
+  // is odd.
+  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt, const uint32_t (&wo)[2][NBW],
+                                                const uint64_t (&jmask)[NBW], int gfirst, int G, bool live) {
     const uint64_t mask = live_mask(live);
     const uint32_t goff = (uint32_t)min(gfirst + ((threadIdx.x & 15) >> 3), G - 1) * 64u;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) vm_load16_nt(w[h][j], wt, wo[h][j] + goff, mask);
+      for (int j = 0; j < NBW; ++j) vm_load16_nt(w[h][j], wt, wo[h][j] + goff, mask & jmask[j]);
   }
 
   // MFMA operand of group gfirst + g of block j: lane 16q + i needs column i,
@@ -161,10 +187,11 @@ struct StreamItem {
   }
 
   // Wait until the weights of the stage about to be used have landed: every
-  // stage issues its loads (those past the end with exec = 0), so
-  // exactly D-1 later stages of PER loads each may still be in flight; the
-  // stage's activation rows were issued before its weights.  Then make the
-  // weights readable and meet the other waves.
+  // stage issues its ring loads (those past the end with exec = 0), so
+  // exactly D-1 later stages of PER loads each may still be in flight (scale
+  // loads issued in between only make the wait stricter); the stage's
+  // activation rows and its scale chunk were issued before its weights.
+  // Then make the weights readable and meet the other waves.
   __device__ __forceinline__ static void stage_wait(v4i (&w)[KG][NBW]) {
     wait_vm<(D - 1) * PER>();
 #pragma unroll
@@ -174,36 +201,48 @@ struct StreamItem {
     wg_barrier();
   }
 
-  __device__ __forceinline__ static void run(const GemmArgs& p, uint8_t* lds, int e, int row0,
-                                             int rows, int n0, int R) {
-    const int lane = opaque_lane(), wave = threadIdx.x >> 6;
-    const int kh = wave >> 2, wn = wave & 3;
+  // The item (expert e, rows row0 .. row0+rows-1, blocks of columns n0 ..
+  // n0 + 16*nb - 1); 1 <= nb <= WPK*NBW.
+  __device__ __forceinline__ static void run(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows, int n0,
+                                             int nb, int R) {
+    const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
+    const int kh = KS == 1 ? 0 : uniform(wave / WPK), wn = KS == 1 ? wave : uniform(wave % WPK);
     const int q = lane >> 4, r16 = lane & 15;
     const int K = p.K, N = p.N, G = K >> 7;
-    const int Gh = (G + 1) / 2;
-    const int gbase = kh ? Gh : 0;
-    const int gcount = kh == 0 ? Gh : G - Gh;  // groups of this wave's half
-    const int S = (Gh + KG - 1) / KG;
+    const int gh = (G + KS - 1) / KS;             // groups of part 0 (part 1 has G - gh)
+    const int gcount = kh == 0 ? gh : G - gh;     // groups of this wave's part
+    const int S = (gh + KG - 1) / KG;             // stages
+    const int Sp = (S + D - 1) / D * D;           // padded to whole ring turns
+    const int nlast = min(n0 + 16 * nb, N) - 1;
 
     const uint8_t* xt = p.A + (size_t)row0 * K;
-    uint32_t xo[MB];
+    uint32_t xo[NXL];
+    int xg[NXL], xs[NXL];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int jx = uniform(wave) * MB + i;
-      const int quad = jx % (4 * MB);
+    for (int i = 0; i < NXL; ++i) {
+      const int jx = wave * NXL + i;              // [group][part][quad]
+      const int quad = jx % (4 * MB), rest = jx / (4 * MB);
+      const int h = rest % KS, kg = rest / KS;
+      xg[i] = uniform(h * gh + kg);
+      xs[i] = uniform((kg * KS + h) * 8192 + quad * 512);
       const int r = quad * 4 + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);
       xo[i] = (uint32_t)min(r, rows - 1) * (uint32_t)K + c * 16;
     }
     const uint8_t* wt = p.B + ((size_t)e * N + n0) * (size_t)(K >> 1);
     uint32_t wo[2][NBW];
+    uint64_t jmask[NBW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < NBW; ++j) {
+      const int blk = j * WPK + wn;
+      jmask[j] = blk < nb ? ~0ull : 0ull;
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int n = min(n0 + (wn * NBW + j) * 16 + 8 * h + (r16 & 7), N - 1);
+      for (int h = 0; h < 2; ++h) {
+        const int n = min(n0 + blk * 16 + 8 * h + (r16 & 7), nlast);
         wo[h][j] = (uint32_t)(n - n0) * (uint32_t)(K >> 1) + q * 16;
       }
+    }
+    const int gbase = kh * gh;                    // first group of this wave's part
 
     v4f acc[NBW][MB];
 #pragma unroll
@@ -218,49 +257,49 @@ struct StreamItem {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) wr[u][kg][j] = v4i{0, 0, 0, 0};
 
-    // Every stage issues its loads (past the last stage with exec = 0 and
-    // addresses clamped in range), so each wait is the same constant; the loop
-    // body is D whole stages and the last S % D stages follow it, so no
-    // control-flow path skips a stage and then runs a later one.
+    // Every stage issues its ring loads (past the last stage with exec = 0
+    // and addresses clamped in range), so each wait is the same constant; the
+    // loop body is D whole stages and the stage count is padded to a multiple
+    // of D, so no control-flow path skips a stage and then runs a later one.
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      if (s < S && (s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, s * KG / SC, R);
-      issue_x(xt, xo, lds + (s % NX) * XSLOT, G, min(s, S - 1), s < S);
-      load_w(wr[s], wt, wo, gbase + min(s, S - 1) * KG, G, s < S);
+      if (s < S && (s * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, nlast, gh, s * KG / SC, R);
+      issue_x(xt, xo, xg, xs, lds + s * XSLOT, G, min(s, S - 1), s < S);
+      load_w(wr[s], wt, wo, jmask, gbase + min(s, S - 1) * KG, G, s < S);
     }
 
     auto stage = [&](int s, int u) __attribute__((always_inline)) {
       stage_wait(wr[u]);
       const int sn = s + D;
-      if (sn < S && (sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, sn * KG / SC, R);
-      issue_x(xt, xo, lds + (sn % NX) * XSLOT, G, min(sn, S - 1), sn < S);
+      if (sn < S && (sn * KG) % SC == 0) issue_scales(p, lds, e, row0, rows, n0, nlast, gh, sn * KG / SC, R);
+      issue_x(xt, xo, xg, xs, lds + (sn % NX) * XSLOT, G, min(sn, S - 1), sn < S);
       const uint8_t* slot = lds + (s % NX) * XSLOT;
       v4i wop[KG][NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) pair_operands(wr[u][0][j], wr[u][1][j], wop[0][j], wop[1][j]);
       // the ring slot is free once paired: its next loads go out before the
-      // MFMAs, so two stages stay in flight while this one computes
-      load_w(wr[u], wt, wo, gbase + min(sn, S - 1) * KG, G, sn < S);
+      // MFMAs, so D stages stay in flight while this one computes
+      load_w(wr[u], wt, wo, jmask, gbase + min(sn, S - 1) * KG, G, sn < S);
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
-        const int gl = s * KG + kg;  // group index within this wave's half
+        const int gl = s * KG + kg;               // group index within this wave's part
         if (gl < gcount) {
-          const uint8_t* sbb = lds + P1_SB + ((gl / SC) & 1) * SBS;
-          const uint8_t* sab = lds + SAB + ((gl / SC) & 1) * P1_SABUF;
-          const int gg = gl % SC;
+          const int buf = (gl / SC) % NBUF, gg = gl % SC, sw = sb_word(gl, gbase, G);
+          const uint8_t* sbb = lds + SB0 + buf * SBB + kh * (WIDTH * SC * 4);
+          const uint8_t* sab = lds + SA0 + buf * SAB + kh * (64 * SC * 4);
           int sbv[NBW];
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const int col = (wn * NBW + j) * 16 + r16;
-            sbv[j] = (int)((lds32(sbb + ((kh * WIDTH + col) * SC + gg) * 4) >> (8 * q)) & 0xffu);
+            const int col = (j * WPK + wn) * 16 + r16;
+            sbv[j] = (int)((lds32(sbb + (col * SC + sw) * 4) >> (8 * q)) & 0xffu);
           }
 #pragma unroll
           for (int i = 0; i < MB; ++i) {
             const int m = i * 16 + r16;
-            const uint8_t* xb = slot + kg * P1_XGROUP + kh * 8192 + m * 128;
+            const uint8_t* xb = slot + (kg * KS + kh) * 8192 + m * 128;
             const v4i x0 = lds128(xb + ((q ^ (m & 7)) << 4));
             const v4i x1 = lds128(xb + (((q + 4) ^ (m & 7)) << 4));
-            const float sa = ldsf(sab + ((kh * 64 + m) * SC + gg) * 4);
+            const float sa = ldsf(sab + (m * SC + gg) * 4);
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
               promote(acc[j][i], sa, mfma_group(wop[kg][j], x0, x1, sbv[j]));
@@ -269,13 +308,10 @@ struct StreamItem {
       }
     };
 
-    static_assert(D == 2, "the stage loop below is written for two stages in flight");
-    int s0 = 0;
-    for (; s0 + 2 <= S; s0 += 2) {
-      stage(s0, 0);
-      stage(s0 + 1, 1);
+    for (int s0 = 0; s0 < Sp; s0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) stage(s0 + u, u);
     }
-    if (s0 < S) stage(s0, 0);
     // every load has retired; the ties keep the ring registers reserved until
     // here (a value never read would otherwise be reused while its load is
     // still in flight)
@@ -287,19 +323,26 @@ struct StreamItem {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) tie(wr[u][kg][j]);
 
-    // add the two K halves in LDS (nothing is in flight -- the last wait was
-    // for zero -- and every wave is past its last LDS read after this barrier)
-    __syncthreads();
-    // one per-lane base (the wave's slice of the scratch is a uniform offset),
-    // constant offsets per (unit, row block)
-    v4f* red = reinterpret_cast<v4f*>(lds) + uniform(wn) * (NBW * MB * 64) + lane;
-    if (kh == 1) {
+    if constexpr (KS == 2) {
+      // add the halves through LDS (every wave is past its last ring read
+      // after this barrier): one per-lane base, constant offsets per (block,
+      // row block)
+      wg_barrier();
+      v4f* red = reinterpret_cast<v4f*>(lds) + wn * (NBW * MB * 64) + lane;
+      if (kh == 1) {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < MB; ++i) red[(j * MB + i) * 64] = acc[j][i];
+          for (int i = 0; i < MB; ++i) red[(j * MB + i) * 64] = acc[j][i];
+      }
+      __syncthreads();
+      if (kh == 0) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int i = 0; i < MB; ++i) acc[j][i] += red[(j * MB + i) * 64];
+      }
     }
-    __syncthreads();
     if (kh == 0) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
@@ -308,49 +351,200 @@ struct StreamItem {
           uint16_t* crow = p.C + (size_t)(row0 + m) * N;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const int n = n0 + (wn * NBW + j) * 16 + q * 4;
-            const v4f o = red[(j * MB + i) * 64];
-            if (n < N) store_bf16x4(crow + n, acc[j][i] + o);
+            const int blk = j * WPK + wn;
+            const int n = n0 + blk * 16 + q * 4;
+            if (blk < nb && n < N) store_bf16x4(crow + n, acc[j][i]);
           }
         }
       }
     }
-    __syncthreads();  // red is overwritten by the next item's loads
+    // the next item's first loads overwrite ring slots and scale buffers
+    // (and the reduction scratch) that slower waves may still be reading
+    wg_barrier();
   }
 };
 
 template <int MB>
 __device__ __forceinline__ void stream_item_mb(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows, int n0,
-                                               int nbw, int R) {
-  switch (nbw) {
-    case 1: StreamItem<1, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
-    case 2: StreamItem<2, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
-    case 3: StreamItem<3, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
-    default: if constexpr (stream_max_nbw(MB) >= 4) StreamItem<4, P1_KG, MB>::run(p, lds, e, row0, rows, n0, R); break;
+                                               int nb, int R) {
+  if (nb <= 4 * stream_max_nbw(MB) && nb <= 16) {
+    switch ((nb + 3) >> 2) {
+      case 1: StreamItem<1, MB, 2>::run(p, lds, e, row0, rows, n0, nb, R); break;
+      case 2: StreamItem<2, MB, 2>::run(p, lds, e, row0, rows, n0, nb, R); break;
+      case 3: StreamItem<3, MB, 2>::run(p, lds, e, row0, rows, n0, nb, R); break;
+      default: if constexpr (stream_max_nbw(MB) >= 4) StreamItem<4, MB, 2>::run(p, lds, e, row0, rows, n0, nb, R); break;
+    }
+  } else if (nb <= 24) {
+    StreamItem<3, MB, 1>::run(p, lds, e, row0, rows, n0, nb, R);
+  } else {
+    if constexpr (stream_max_nbw(MB) >= 4) StreamItem<4, MB, 1>::run(p, lds, e, row0, rows, n0, nb, R);
   }
 }
 
-// One streaming item of nbw units (nbw <= stream_max_nbw of its row blocks).
+// One streaming item: nb blocks of 16 columns from column n0, 1 <= nb <=
+// 8 * stream_max_nbw(row blocks).  Items of up to 16 blocks (12 with four row
+// blocks) split K between two halves of the workgroup.
 __device__ __forceinline__ void stream_item(const GemmArgs& p, uint8_t* lds, int e, int row0, int rows, int n0,
-                                            int nbw, int R) {
+                                            int nb, int R) {
   switch ((rows + 15) >> 4) {
-    case 1: stream_item_mb<1>(p, lds, e, row0, rows, n0, nbw, R); break;
-    case 2: stream_item_mb<2>(p, lds, e, row0, rows, n0, nbw, R); break;
-    case 3: stream_item_mb<3>(p, lds, e, row0, rows, n0, nbw, R); break;
-    default: stream_item_mb<4>(p, lds, e, row0, rows, n0, nbw, R); break;
+    case 1: stream_item_mb<1>(p, lds, e, row0, rows, n0, nb, R); break;
+    case 2: stream_item_mb<2>(p, lds, e, row0, rows, n0, nb, R); break;
+    case 3: stream_item_mb<3>(p, lds, e, row0, rows, n0, nb, R); break;
+    default: stream_item_mb<4>(p, lds, e, row0, rows, n0, nb, R); break;
   }
 }
 
-// Items dealt round-robin (experts of different row blocks).  Expert e's
-// items are w = min(W, stream_max_nbw(its row blocks)) units wide, with the
-// cap W that minimises rounds x per-item bytes, per-item bytes ~ weights (32
-// per unit per K) plus activation rows (about 32 per K): wider items re-read
-// the activation rows less often and pay the pipeline fill and drain fewer
-// times, narrower ones spread few experts over more workgroups.  Items are
-// numbered in decreasing order of their cost, w * (4 + row blocks), in four
-// classes (the row blocks), and dealt in a snake order (round r gives
-// workgroup b item r*G + b for even r, r*G + G-1-b for odd r), so that a
-// workgroup's second item is light when its first was heavy.
+// Workgroup order that keeps neighbours on one XCD: consecutive workgroup
+// numbers go to the eight XCDs in turn, so workgroups b, b + 8, b + 16, ...
+// share an XCD (and its L2); numbering them consecutively gives the
+// workgroups of one expert one XCD, whose L2 then fetches that expert's
+// activation rows once.
+__device__ __forceinline__ int xcd_rank(int b, int grid) {
+  if ((grid & 7) != 0) return b;
+  return (b & 7) * (grid >> 3) + (b >> 3);
+}
+
+// Work split when there are no more streaming experts than workgroups.
+// Every block costs the same weight bytes, but a stage costs more than its
+// bytes (the barrier, the loads issued after it, the MFMAs, more of them with
+// more row blocks), so a block of an expert with more row blocks takes longer,
+// and a workgroup should run its blocks as one item (at most 8 *
+// stream_max_nbw(row blocks) blocks).  Per-block weights 16, 17, 22 and 25
+// for 1-4 row blocks: per-stage timestamps on the decode gate/up workload
+// read 2.6 us per stage of about 30 blocks with one or two row blocks, 2.85
+// with three and 2.65 per stage of 24 blocks with four, and a sweep of the
+// weights around those ratios (back-to-back launches) measured these fastest.  Streaming expert t (in tile order) gets one
+// workgroup plus its weight's share of the other grid - tiles workgroups of
+// the XCD-grouped order,
+//   first(t) = t + floor(Wcum(t) * (grid - tiles) / Wtot),
+// and splits its NB blocks evenly among them.  Wave 0 writes, for t <= tiles,
+//   s_tab[t]             first(t) (first(tiles) = grid)
+//   s_tab[ST_EXP + t]    expert of tile t
+// so that a workgroup finds its tile with one compare per lane.  Every thread
+// must call it; 32-bit arithmetic throughout (Wtot < 2^16, grid < 2^12).
+constexpr int ST_EXP = 1024;
+__device__ __forceinline__ int stream_block_weight(int rows) {
+  const int mb = (rows + 15) >> 4;
+  return mb == 1 ? 16 : mb == 2 ? 17 : mb == 3 ? 22 : 25;
+}
+__device__ __forceinline__ void stream_alloc(const int* s_off, const int* s_sbase, int E, int grid, int* s_tab) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (E + 63) / 64;
+    const int i0 = lane * per;
+    int sum = 0;
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) sum += stream_block_weight(rows);
+      }
+    }
+    const int incl = wave_inclusive_sum(sum);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane(incl, 63);
+    const int tiles = s_sbase[E];
+    const uint32_t spare = (uint32_t)(grid - tiles);
+    uint32_t run = (uint32_t)(incl - sum);
+    for (int k = 0; k < per; ++k) {
+      const int e = i0 + k;
+      if (e < E) {
+        const int rows = s_off[e + 1] - s_off[e];
+        if (rows > 0 && rows <= S_MAX) {
+          const int t = s_sbase[e];
+          s_tab[t] = t + (int)(run * spare / wtot);
+          s_tab[ST_EXP + t] = e;
+          run += (uint32_t)stream_block_weight(rows);
+        }
+      }
+    }
+    if (lane == 0) s_tab[tiles] = grid;
+  }
+  __syncthreads();
+}
+
+// Workgroup b's expert e and its block range [b0, b1) (see above).
+__device__ __forceinline__ void stream_expert_range(const int* s_tab, int tiles, int NB, int b, int grid, int* e,
+                                                    int* b0, int* b1) {
+  const int v = xcd_rank(b, grid);
+  const int lane = threadIdx.x & 63;
+  int t = 0;
+  for (int x0 = 0; x0 < tiles; x0 += 64) {
+    const int x = x0 + lane;
+    const uint64_t m = __ballot(x < tiles && s_tab[x] <= v && v < s_tab[x + 1]);
+    if (m) t = x0 + (int)__builtin_ctzll(m);
+  }
+  t = uniform(t);
+  *e = uniform(s_tab[ST_EXP + t]);
+  const int s0 = uniform(s_tab[t]);
+  const uint32_t k = (uint32_t)(uniform(s_tab[t + 1]) - s0);  // >= 1
+  const uint32_t j = (uint32_t)(v - s0);
+  *b0 = (int)((uint32_t)NB * j / k);
+  *b1 = (int)((uint32_t)NB * (j + 1) / k);
+}
+
+// The same split for pools of fewer than 64 experts, computed by every wave
+// in registers (lane e holds expert e; one scan per quantity, one ballot), so
+// that a workgroup's first loads do not wait for LDS tables and barriers:
+// the offsets are checked (offsets[0] = 0, nondecreasing), then the
+// workgroup's streaming expert and block range are found as above, and
+// whether any expert needs the MFMA phase.  grid must be at least 64 (so that
+// tiles <= E < grid) and below 4096 (32-bit products).
+struct StreamAssign {
+  bool valid;      // offsets usable
+  bool any_mfma;   // some expert has more than S_MAX rows
+  int tiles;       // streaming experts
+  int e, b0, b1;   // this workgroup's expert and blocks (tiles > 0)
+  int row0, rows;  // that expert's rows
+  int R;           // offsets[E]
+};
+__device__ __forceinline__ StreamAssign stream_assign_small(const int32_t* __restrict__ offsets, int E, int NB, int b,
+                                                            int grid) {
+  StreamAssign a;
+  const int lane = threadIdx.x & 63;
+  const int lo = lane <= E ? offsets[lane] : 0;
+  const int hi = __shfl_down(lo, 1, 64);         // offsets[lane + 1] for lane < E
+  const bool in = lane < E;
+  const int rows = in ? hi - lo : 0;
+  a.valid = __ballot((lane == 0 && lo != 0) || (in && rows < 0)) == 0;
+  a.R = __builtin_amdgcn_readlane(lo, E);
+  a.any_mfma = __ballot(in && rows > S_MAX) != 0;
+  const bool st = in && rows > 0 && rows <= S_MAX;
+  const int w = st ? stream_block_weight(rows) : 0;
+  const int winc = wave_inclusive_sum(w);
+  const int tinc = wave_inclusive_sum(st ? 1 : 0);
+  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane(winc, 63);
+  a.tiles = __builtin_amdgcn_readlane(tinc, 63);
+  a.e = a.b0 = a.b1 = a.row0 = a.rows = 0;
+  if (!a.valid || a.tiles == 0) return a;
+  const uint32_t spare = (uint32_t)(grid - a.tiles);
+  // first workgroup of this lane's expert and of the next streaming expert
+  const int f0 = tinc - (st ? 1 : 0) + (int)((uint32_t)(winc - w) * spare / wtot);
+  const int f1 = tinc + (int)((uint32_t)winc * spare / wtot);
+  const int v = xcd_rank(b, grid);
+  const uint64_t m = __ballot(st && f0 <= v && v < f1);
+  const int el = (int)__builtin_ctzll(m);       // exactly one lane holds v
+  a.e = el;
+  const int s0 = __builtin_amdgcn_readlane(f0, el);
+  const uint32_t k = (uint32_t)(__builtin_amdgcn_readlane(f1, el) - s0);
+  const uint32_t j = (uint32_t)(v - s0);
+  a.b0 = (int)((uint32_t)NB * j / k);
+  a.b1 = (int)((uint32_t)NB * (j + 1) / k);
+  a.row0 = __builtin_amdgcn_readlane(lo, el);
+  a.rows = __builtin_amdgcn_readlane(rows, el);
+  return a;
+}
+
+// Items dealt round-robin (more streaming experts than workgroups).  A unit
+// is 128 columns (8 blocks); expert e's items are w = min(W, stream_max_nbw
+// of its row blocks) units wide, with the cap W that minimises rounds x
+// per-item bytes, per-item bytes ~ weights (64 per unit per K) plus
+// activation rows (up to 64 per K): wider items re-read the activation rows
+// less often and pay the pipeline fill and drain fewer times, narrower ones
+// spread few experts over more workgroups.  Items are numbered in decreasing
+// order of their cost, w * (4 + row blocks), in four classes (the row
+// blocks), and dealt in a snake order (round r gives workgroup b item r*G +
+// b for even r, r*G + G-1-b for odd r), so that a workgroup's second item is
+// light when its first was heavy.
 //   s_eord[k]   expert at class-ordered position k
 //   s_rrc[r]    class of rank r: {first item, first position, items per expert, width}
 //   s_rrc[4][0] total items
@@ -393,7 +587,7 @@ __device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, 
       int items = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) items += tot[j] * ipd[min(w, stream_max_nbw(j + 1)) - 1];
-      const float cost = ceilf((float)items / (float)grid) * (float)(32 * w + 32);
+      const float cost = ceilf((float)items / (float)grid) * (float)(64 * w + 64);
       if (best_cost < 0.f || cost <= best_cost) {
         best_cost = cost;
         W = w;
@@ -456,34 +650,5 @@ __device__ __forceinline__ void stream_rr_plan(const int* s_off, int E, int nu, 
   }
   __syncthreads();
 }
-
-// Work split of the streaming phase when every streaming tile has the same
-// row blocks and there are at least two units per workgroup: the contiguous
-// range [*u0, *u1) of the
-// U = tiles * nu units of 64 columns (unit u = column block u % nu of
-// streaming m-tile u / nu) that workgroup b of `grid` streams.  Every expert
-// tile's units cost the same weight bytes whatever its rows, so
-//   tiles < grid:  tile t gets workgroups [t*grid/tiles, (t+1)*grid/tiles)
-//                  (21 or 22 each at 12 tiles on 256 CUs) and splits its nu
-//                  units evenly among them: no range spans two experts;
-//   tiles >= grid: workgroup b gets units [U*b/grid, U*(b+1)/grid).
-// A range is run as items of at most P1_RANGE_MAXNBW units that never span two
-// experts.  Against dealing fixed 192-column items round-robin this lowers
-// the largest share (E=12, 64 routed rows, N=6144: 5 units instead of 6).
-__device__ __forceinline__ void stream_range(int tiles, int nu, int b, int grid, long long* u0, long long* u1) {
-  if (tiles < grid) {
-    const int t = (int)(((long long)(b + 1) * tiles - 1) / grid);
-    const int s0 = (int)((long long)t * grid / tiles);
-    const int k = (int)((long long)(t + 1) * grid / tiles) - s0;  // >= 1 since grid > tiles
-    const int j = b - s0;
-    *u0 = (long long)t * nu + (long long)j * nu / k;
-    *u1 = (long long)t * nu + (long long)(j + 1) * nu / k;
-  } else {
-    const long long U = (long long)tiles * nu;
-    *u0 = U * b / grid;
-    *u1 = U * (b + 1) / grid;
-  }
-}
-
 
 }  // namespace w4a8

@@ -199,6 +199,13 @@ DECODE_ROWS = [0, 0, 1, 3, 5, 5, 6, 6, 7, 7, 7, 8, 9, 9, 11, 14, 15, 15, 16, 17,
     ([40] * 3 + [0] + [33] * 2, 8192, 640),
     (list(range(0, 140, 7)), 256, 1152),
     ([3], 32, 896),
+    # about one workgroup per expert (200 experts of 1-4 row blocks): each
+    # workgroup's range of 64 blocks runs as two or three items
+    ([9, 33, 50, 2] * 50, 1024, 384),
+    # narrow items split K between the two halves of the workgroup: 10
+    # blocks per workgroup with four row blocks, 16 with two (odd group count)
+    ([60] * 40, 1024, 384),
+    ([20] * 16, 4096, 640),
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)

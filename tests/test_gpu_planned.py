@@ -1,8 +1,12 @@
 """GPU grouped GEMM over a tile list built beforehand
 (w4a8_grouped_gemm_planned).
 
-* With w4a8_plan's own plan it must equal w4a8_grouped_gemm bit for bit (the
-  same kernels; results do not depend on the item widths or the split).
+* With w4a8_plan's own plan it must equal w4a8_grouped_gemm bit for bit on
+  the rows of MFMA-class experts (the same tile kernel), and meet the parity
+  bar everywhere: streaming items are split differently by the two kernels
+  (per-expert column ranges against fixed 512-column items), and a narrow
+  item adds its two K halves at the end where a wide one walks K in one
+  pass, so the fp32 sums of streaming rows may round differently.
 * Over the wide shared expert pools of MoonEP PR #38 (performance table:
   3072 and 6144 experts), beyond the plain GEMM's 2048, rows from the GPU
   route prep: parity with the oracle.
@@ -51,7 +55,7 @@ def _case(counts, N, K, seed):
 
 
 @pytest.mark.parametrize("layout", [0, 1])
-def test_planned_equals_plain(gpu_lib, layout):
+def test_planned_matches_plain(gpu_lib, layout):
     for counts, N, K in [(MIXED, 320, 384), ([5] * 300, 192, 128), ([40] * 3 + [0] + [33] * 2, 1024, 256)]:
         A, SA, B, SB, off = _case(counts, N, K, sum(counts) + N)
         SA_l = (SA if layout == 0 else synth.to_m_major(SA)).cuda()
@@ -60,7 +64,16 @@ def test_planned_equals_plain(gpu_lib, layout):
         plan = gpu_lib.plan(d[3], len(counts), N, K, max_total_rows=int(off[-1]))
         C1 = gpu_lib.grouped_gemm_planned(d[0], SA_l, layout, d[1], d[2], d[3], plan)
         torch.cuda.synchronize()
-        assert np.array_equal(bits_of(C0), bits_of(C1)), (counts[:4], N, K)
+        b0, b1 = bits_of(C0), bits_of(C1)
+        mfma_rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in range(len(counts))
+                                    if off[e + 1] - off[e] > 64] + [np.zeros(0, dtype=np.int64)])
+        assert np.array_equal(b0[mfma_rows], b1[mfma_rows]), (counts[:4], N, K)
+        ex = grouped_gemm_f64(A, SA_l.cpu().reshape(-1), layout, B, SB, off)
+        mag = grouped_gemm_f64(A, SA_l.cpu().reshape(-1), layout, B, SB, off, absolute=True)
+        for name, bits in (("plain", b0), ("planned", b1)):
+            assert_parity(bits, bf16_rne_bits(ex), f"{name} {counts[:4]} N={N} K={K} layout={layout}",
+                          exact=ex, abs_sum=mag, K=K, group_eps=GROUP_EPS_RANDOM_CODES)
+        print(f"streaming rows equal bit for bit: {np.array_equal(b0, b1)}", flush=True)
 
 
 @pytest.mark.parametrize("E,T,skew", [(3072, 16384, False), (6144, 2048, True), (6144, 16384, False)])
