@@ -163,14 +163,18 @@ struct StreamItem {
   // column; wo = this lane's column offsets; jmask[j] = exec of block j (0
   // past the item's end); the second group is clamped to the last one when G
   // is odd.
-  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt, const uint32_t (&wo)[2][NBW],
-                                                const uint64_t (&jmask)[NBW], int gfirst, int G, bool live) {
+  __device__ __forceinline__ static void load_wh(int h, v4i (&w)[KG][NBW], const uint8_t* wt,
+                                                 const uint32_t (&wo)[2][NBW], const uint64_t (&jmask)[NBW], int gfirst,
+                                                 int G, bool live) {
     const uint64_t mask = live_mask(live);
     const uint32_t goff = (uint32_t)min(gfirst + ((threadIdx.x & 15) >> 3), G - 1) * 64u;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) vm_load16_nt(w[h][j], wt, wo[h][j] + goff, mask & jmask[j]);
+    for (int j = 0; j < NBW; ++j) vm_load16_nt(w[h][j], wt, wo[h][j] + goff, mask & jmask[j]);
+  }
+  __device__ __forceinline__ static void load_w(v4i (&w)[KG][NBW], const uint8_t* wt, const uint32_t (&wo)[2][NBW],
+                                                const uint64_t (&jmask)[NBW], int gfirst, int G, bool live) {
+    load_wh(0, w, wt, wo, jmask, gfirst, G, live);
+    load_wh(1, w, wt, wo, jmask, gfirst, G, live);
   }
 
   // MFMA operand of group gfirst + g of block j: lane 16q + i needs column i,
@@ -277,11 +281,12 @@ struct StreamItem {
       v4i wop[KG][NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) pair_operands(wr[u][0][j], wr[u][1][j], wop[0][j], wop[1][j]);
-      // the ring slot is free once paired: its next loads go out before the
-      // MFMAs, so D stages stay in flight while this one computes
-      load_w(wr[u], wt, wo, jmask, gbase + min(sn, S - 1) * KG, G, sn < S);
+      // the ring slot is free once paired: its next loads go out in two
+      // halves, each before one group's MFMAs, so D stages stay in flight
+      // while this one computes and the issue is spread over the stage
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
+        load_wh(kg, wr[u], wt, wo, jmask, gbase + min(sn, S - 1) * KG, G, sn < S);
         const int gl = s * KG + kg;               // group index within this wave's part
         if (gl < gcount) {
           const int buf = (gl / SC) % NBUF, gg = gl % SC, sw = sb_word(gl, gbase, G);

@@ -65,8 +65,9 @@ def test_planned_matches_plain(gpu_lib, layout):
         C1 = gpu_lib.grouped_gemm_planned(d[0], SA_l, layout, d[1], d[2], d[3], plan)
         torch.cuda.synchronize()
         b0, b1 = bits_of(C0), bits_of(C1)
-        mfma_rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in range(len(counts))
-                                    if off[e + 1] - off[e] > 64] + [np.zeros(0, dtype=np.int64)])
+        o = np.asarray(off.cpu().numpy() if hasattr(off, "cpu") else off, dtype=np.int64)
+        mfma_rows = np.concatenate([np.arange(o[e], o[e + 1]) for e in range(len(counts))
+                                    if o[e + 1] - o[e] > 64] + [np.zeros(0, dtype=np.int64)])
         assert np.array_equal(b0[mfma_rows], b1[mfma_rows]), (counts[:4], N, K)
         ex = grouped_gemm_f64(A, SA_l.cpu().reshape(-1), layout, B, SB, off)
         mag = grouped_gemm_f64(A, SA_l.cpu().reshape(-1), layout, B, SB, off, absolute=True)
