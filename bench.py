@@ -43,8 +43,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 
 METRIC = "grouped W4A8 GEMM us + TFLOP/s at M=64/1152/16384, % of MFMA/HBM roofline"
 HEADLINE = ("decode_gateup", 0)
-# the other workloads of the metric, measured before the headline (whose
-# timed steps then run at settled clocks)
+# the other workloads of the metric, measured after the headline
 SUITE = (("prefill_gateup", 1), ("prefill_down", 0), ("prefill_down", 1),
          ("e12_w13_m8", 0), ("e12_w13_m64", 0), ("e12_w2_m8", 0), ("e12_w2_m64", 0))
 BOUND = {"prefill_gateup": "mfma", "prefill_down": "mfma"}
@@ -671,6 +670,47 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    # the headline workload first, on a device that has run nothing else yet
+    # (later workloads allocate and free tens of GB): untimed GEMM launches
+    # until about 20 ms of work has run so that clocks settle (W = 5 steps are
+    # 0.4 ms), then W untimed warmup steps, then exactly K timed steps
+    log(f"{name} layout {layout}: generating")
+    w = Workload(name, layout, dev)
+    log(f"inputs resident: R={w.p.R} N={w.p.N} K={w.p.K} E={w.p.E}, {w.nrot} weight copies")
+    w.route()
+    settle = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_settle = 0
+    settle[0].record()
+    while True:
+        for i in range(20):
+            w.gemm(n_settle + i)
+        n_settle += 20
+        settle[1].record()
+        torch.cuda.synchronize()
+        if settle[0].elapsed_time(settle[1]) >= 20.0 or n_settle >= 4000:
+            break
+    for i in range(warmup):
+        w.step(i)
+    torch.cuda.synchronize()
+    log(f"{n_settle} settling launches, warmup done ({warmup} steps)")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        w.step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+    # per-launch timing of the grouped GEMM call, on the stream it is launched
+    # on, launches queued back to back (the routing prep's offsets do not
+    # change between steps; with a prep before every launch the host's two
+    # calls per step outlast the E=12 launches and the events would time
+    # the host)
+    gemm_ms = time_launches(w.gemm, max(steps, 20), warmup=0)
+    log(f"timed {steps} steps: {ms_per_step * 1e3:.1f} us/step, gemm median "
+        f"{statistics.median(gemm_ms) * 1e3:.2f} us")
+
     probes = None
     if not args.no_probes:
         from moe_grouped_precision_amd import probe
@@ -680,6 +720,10 @@ def main():
                   "mfma_fp4xfp8_zero_acc_tflops": round(probe.mfma_promote_tflops(False), 1),
                   "mfma_fp4xfp8_zero_acc_promote_tflops": round(probe.mfma_promote_tflops(True), 1),
                   "hbm_read_gbs": round(probe.read_gbs(), 1)}
+    head = w.report(gemm_ms, probes)
+    head["settling_launches"] = n_settle
+    p_head, off_head = w.p, w.off_d.cpu().numpy()
+    w.free()
 
     configs = {}
     if suite:
@@ -700,38 +744,12 @@ def main():
                   "grouped_gemm_wide_pool": measure_gemm_wide_pool(),
                   "grouped_gemm_planned_wide_pool": measure_gemm_planned_wide_pool()}
 
-    # the headline workload: W untimed steps, then K timed steps
-    log(f"{name} layout {layout}: generating")
-    w = Workload(name, layout, dev)
-    log(f"inputs resident: R={w.p.R} N={w.p.N} K={w.p.K} E={w.p.E}, {w.nrot} weight copies")
-    for i in range(warmup):
-        w.step(i)
-    torch.cuda.synchronize()
-    log(f"warmup done ({warmup} steps)")
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        w.step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / steps
-    # per-launch timing of the grouped GEMM call, on the stream it is launched
-    # on, launches queued back to back (the routing prep's offsets do not
-    # change between steps; with a prep before every launch the host's two
-    # calls per step outlast the E=12 launches and the events would time
-    # the host)
-    gemm_ms = time_launches(w.gemm, steps, warmup=0)
-    head = w.report(gemm_ms, probes)
-    log(f"timed {steps} steps: {ms_per_step * 1e3:.1f} us/step, gemm median {head['gemm_us']['median']} us")
-
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w.p, w.off_d.cpu().numpy(), layout, args.cpu_budget)
+        cpu = cpu_baseline(p_head, off_head, layout, args.cpu_budget)
 
-    p = w.p
+    p = p_head
     flops = 2.0 * p.R * p.N * p.K
     config = {"workload": head["workload"]}
     config.update({k: v for k, v in head.items() if k not in ("workload", "roofline")})
