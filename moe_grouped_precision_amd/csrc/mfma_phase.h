@@ -24,7 +24,7 @@ namespace w4a8 {
 //   X ring   : 6 slots (three pairs of groups) x [128 rows][128 B]
 //              (row chunk c at c ^ xkey(row))
 //   SB chunk : 2 x [512 cols][SC] u32  (E8M0 codes of groups SC*c .. SC*c+3,
-//              word gg of column n at gg ^ skey(n))
+//              word gg of column n at n * SC + gg)
 //   SA chunk : 2 x [128 rows][SC] fp32 (word gg of row r at gg ^ skey(r))
 // The K loop runs in pairs of groups with one barrier per pair (a barrier per
 // group measured 2-3% slower): wait for the weights of the pair's first group,
@@ -53,7 +53,7 @@ constexpr int P2_BYTES = P2_SA + 2 * P2_SABUF;
 constexpr int P2_X_OPS = MF_BM * 128 / 1024 / MF_WAVES;  // activation loads per wave per stage
 static_assert(MF_BN == 64 * MF_WAVES, "each wave owns 64 columns");
 static_assert(P2_X_OPS * 1024 * MF_WAVES == MF_BM * 128, "activation loads cover the slot");
-static_assert(MF_BN * SC == MF_WAVES * 4 * 64, "four 4-byte E8M0 loads per lane cover a chunk");
+static_assert(MF_BN == MF_WAVES * 64, "one 16-byte E8M0 load per column covers a chunk");
 static_assert(MF_BM * SC == MF_WAVES * 64, "one 4-byte activation-scale load per lane covers a chunk");
 // a scale chunk (two pairs) is refilled during the pair two before its first
 // one, after every pair of the chunk two back has passed that pair's barrier
@@ -157,26 +157,43 @@ struct MfmaTile {
              lds_u32(lds + (g % P2_NX) * P2_XSLOT + (wave * P2_X_OPS + i) * 1024), live_mask(g < G));
   }
 
-  // Scale chunk c: 512 columns x SC groups of E8M0 words (four 4-byte loads
-  // per wave) and 128 rows x SC groups of activation scales (one per wave).
-  // Four lanes read one column's (row's) 16 contiguous bytes; word gg of a
-  // column (row) r lands at position gg ^ skey(r).  (One 16-byte load per
-  // lane instead, four times fewer instructions, measured slower.)
+  // Scale chunk c (groups SC*c .. SC*c+3).  E8M0: a column's codes of SC
+  // consecutive groups are 16 contiguous bytes, so one 16-byte load per column
+  // (wave w: columns 64w .. 64w+63), word gg of column n at n * SC + gg (a
+  // 4-byte read of 16 consecutive columns then hits 16 distinct banks); the
+  // load starts at group SC*c clamped to G - SC so that it stays inside the
+  // column, and the word of group g then sits at g - load start (sb_word).
+  // With fewer than SC groups in all, four 4-byte loads per wave, groups
+  // clamped.  Activation scales: 128 rows x SC groups, one 4-byte load per
+  // lane; four lanes read one row's SC words (row-major) and word gg of row r
+  // lands at position gg ^ skey(r).
   __device__ __forceinline__ void load_scales(int c) const {
     const int lane = opaque_lane(), wave = uniform(threadIdx.x >> 6);
     const int K = p.K, N = p.N;
+    if (G >= SC) {
+      const int col = wave * 64 + lane;
+      const int n = FUSED ? fused_col(n0, col, p.I) : min(n0 + col, N - 1) - n0;
+      const int g = min(SC * c, G - SC);
+      const uint8_t* base = p.SB + ((size_t)e * N + (FUSED ? 0 : n0)) * (size_t)(K >> 5) + (size_t)g * 4;
+      vm_dma16(base, (uint32_t)n * (uint32_t)(K >> 5), lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + wave * 1024),
+               live_mask(true));
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = ((wave * 4 + i) * 64 + lane) >> 2;  // rows [col] of SC words
-      const int g = min(SC * c + ((lane & 3) ^ skey<SC>(col)), G - 1);
-      const int n = FUSED ? fused_col(n0, col, p.I) : min(n0 + col, N - 1);
-      vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
-              lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
+      for (int i = 0; i < 4; ++i) {
+        const int col = ((wave * 4 + i) * 64 + lane) >> 2;
+        const int g = min(SC * c + (lane & 3), G - 1);
+        const int n = FUSED ? fused_col(n0, col, p.I) : min(n0 + col, N - 1);
+        vm_dma4(p.SB + ((size_t)e * N + n) * (size_t)(K >> 5) + (size_t)g * 4,
+                lds_u32(lds + P2_SB + (c & 1) * P2_SBBUF + (wave * 4 + i) * 256));
+      }
     }
     const int r = (wave * 64 + lane) >> 2;  // rows [row] of SC words
     const int g = min(SC * c + ((lane & 3) ^ skey<SC>(r)), G - 1);
     const size_t row = (size_t)row0 + min(r, rows - 1);
     vm_dma4(sa_ptr(p, row, g, G, R), lds_u32(lds + P2_SA + (c & 1) * P2_SABUF + wave * 256));
+  }
+  __device__ __forceinline__ int sb_word(int g) const {
+    return (g % SC) + (G >= SC ? max(0, SC * (g / SC) - (G - SC)) : 0);
   }
 
   // One K group: step mi issues the LDS reads of block mi+1 and the four
@@ -229,11 +246,9 @@ struct MfmaTile {
     const uint8_t* sab = lds + P2_SA + ((g / SC) & 1) * P2_SABUF;
     const int gg = g % SC;
     const int k0 = gg ^ (r16 >> 3);
-    const uint8_t* sbl0 = sbb + ((wn * 64 + r16) * SC + k0) * 4;
-    const uint8_t* sbl1 = sbb + ((wn * 64 + r16) * SC + (k0 ^ 2)) * 4;
+    const uint8_t* sbl = sbb + ((wn * 64 + r16) * SC + sb_word(g)) * 4;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      sbv[nb] = (int)((lds32(((nb & 1) ? sbl1 : sbl0) + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
+    for (int nb = 0; nb < 4; ++nb) sbv[nb] = (int)((lds32(sbl + nb * 16 * SC * 4) >> (8 * q)) & 0xffu);
     a.x0 = slot + xl0;
     a.x1 = slot + xl1;
     a.sa0 = sab + (r16 * SC + k0) * 4;
