@@ -206,6 +206,10 @@ DECODE_ROWS = [0, 0, 1, 3, 5, 5, 6, 6, 7, 7, 7, 8, 9, 9, 11, 14, 15, 15, 16, 17,
     # blocks per workgroup with four row blocks, 16 with two (odd group count)
     ([60] * 40, 1024, 384),
     ([20] * 16, 4096, 640),
+    # either side of the register-only split (pools under 64 experts) and the
+    # LDS-table split: 63 and 64 experts of mixed sizes, empty ones included
+    ([17, 40, 3, 0, 64, 9, 80] * 9, 1024, 384),
+    ([17, 40, 3, 0, 64, 9, 80] * 9 + [33], 1024, 384),
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
