@@ -270,7 +270,8 @@ int w4a8_grouped_gemm(const uint8_t* A_fp8_dev, const float* a_scales_dev, int a
  * are then not written), so no plan makes the kernel touch memory outside
  * A, a_scales, B, b_scales and C.  A plan whose status word is not 0 makes
  * the kernel write nothing.  Streaming tiles are dealt as items of up to
- * three 64-column units, MFMA tiles as 512-column items.  The other
+ * 512 columns (split further where the tile's rows leave fewer registers
+ * per column), MFMA tiles as 512-column items.  The other
  * arguments, layouts, numerics and limits are those of w4a8_grouped_gemm,
  * except 1 <= E <= W4A8_MAX_PREP_EXPERTS.  plan_bytes below the header ->
  * W4A8_ERR_CAPACITY.

@@ -38,7 +38,7 @@ import numpy as np
 GRAN = 16          # m granularity: rows of one MFMA block
 S_MAX = 64         # largest expert served by the weight-streaming class
 T_MAX = 128        # largest m-tile of the MFMA class
-TN_STREAM = 64     # n granularity of streaming work (a workgroup item holds 1-3 of them)
+TN_STREAM = 64     # n granularity by which the plan counts streaming work
 TN_MFMA = 512      # n width of one MFMA work item
 
 CLASS_NONE, CLASS_STREAM, CLASS_MFMA = 0, 1, 2
