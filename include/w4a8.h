@@ -96,9 +96,12 @@ enum {
  * workgroup's chunk, each with its own copy of per-expert counts; W is the
  * largest of 16, 15, ..., 1 that fits the device's per-workgroup LDS (the
  * fit of MoonEP PR #38, change section, applied to the ranking copies: the
- * other waves need no LDS, so the workgroup keeps all 16).  When not even
- * one copy fits (E above 13648 on a 160 KB device) the call returns
- * W4A8_ERR_CAPACITY before any launch.  The result does not depend on W.
+ * other waves need no LDS, so the workgroup keeps all 16).  A batch of fewer
+ * than 1024 slots uses at most one ranking wave per 64 slots, and the
+ * workgroup then holds only those waves and one per 64 experts (at most 16).
+ * When not even one copy fits (E above 13648 on a 160 KB device) the call
+ * returns W4A8_ERR_CAPACITY before any launch.  The result does not depend on
+ * W or on the number of waves.
  * Alignment: 4 bytes for every pointer.
  */
 int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E,
@@ -108,7 +111,8 @@ int w4a8_route_prep(const int32_t* topk_ids_dev, int T, int top_k, int E,
 /*
  * w4a8_route_prep_waves -- host only, no device work: the ranking waves per
  * workgroup w4a8_route_prep uses for E experts on a device whose workgroups
- * may hold lds_limit_bytes of LDS (the largest W in 16..1 with
+ * may hold lds_limit_bytes of LDS, for batches of at least 1024 slots (the
+ * largest W in 16..1 with
  * 4 * ((W + 2) * E + 16) <= lds_limit_bytes).  Returns 0 when no W fits (the
  * route prep then returns W4A8_ERR_CAPACITY) or E is outside
  * [1, W4A8_MAX_PREP_EXPERTS].

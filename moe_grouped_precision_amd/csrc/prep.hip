@@ -14,12 +14,14 @@
 // (MoonEP PR #38, change section: drop one wave at a time from the largest
 // workgroup, report resource overflow when even one wave does not fit), which
 // carries the prep to thousands of experts.
+#include <algorithm>
+
 #include "w4a8_device.h"
 #include "w4a8_launch.h"
 
 namespace w4a8 {
 
-// B workgroups of ROUTE_MAX_WAVES waves; workgroup b owns the contiguous
+// B workgroups of up to ROUTE_MAX_WAVES waves; workgroup b owns the contiguous
 // slots [b*chunk, (b+1)*chunk) and writes their rows.  The first wr waves
 // rank (each one span of the chunk, with its own copy of the chunk's
 // counts); all waves histogram and scan.  Every workgroup histograms
@@ -248,7 +250,13 @@ hipError_t launch_route_prep(const int32_t* ids, int n, int E, int W, int32_t* c
   int chunk = kMinChunk;
   if ((n + chunk - 1) / chunk > kMaxBlocks) chunk = ((n + kMaxBlocks - 1) / kMaxBlocks + 63) & ~63;
   const int blocks = n > 0 ? (n + chunk - 1) / chunk : 1;
-  hipLaunchKernelGGL(route_prep_kernel, dim3(blocks), dim3(ROUTE_MAX_WAVES * 64), route_prep_lds_bytes(E, W),
+  // a small batch: no more ranking waves than its 64-id spans (the per-expert
+  // prefix over waves is serial in W), and no more waves in all than those
+  // and one per 64 experts (phase 2's threads), so the workgroup's barriers
+  // and scans are short; the row map does not depend on either
+  W = std::min(W, std::max(1, (std::min(n, chunk) + 63) / 64));
+  const int threads = 64 * std::max(W, std::min(ROUTE_MAX_WAVES, (E + 63) / 64));
+  hipLaunchKernelGGL(route_prep_kernel, dim3(blocks), dim3(threads), route_prep_lds_bytes(E, W),
                      stream, ids, n, E, nbits, chunk, W, counts, offsets, row_of_slot);
   return hipGetLastError();
 }

@@ -24,10 +24,10 @@ struct GemmArgs {
   int max_tiles;
 };
 
-// Route prep: the workgroup holds ROUTE_MAX_WAVES waves, W of which rank
-// (1..ROUTE_MAX_WAVES), and route_prep_lds_bytes(E, W) bytes of LDS;
+// Route prep: the workgroup holds up to ROUTE_MAX_WAVES waves, W of which
+// rank (1..ROUTE_MAX_WAVES), and route_prep_lds_bytes(E, W) bytes of LDS;
 // route_prep_waves picks the largest W that fits lds_limit bytes, 0 if none
-// does.
+// does, and the launch lowers W (and the waves) for batches of few ids.
 constexpr int ROUTE_MAX_WAVES = 16;
 constexpr int ROUTE_LOADS = 16;  // 16-byte id loads in flight per lane
 size_t route_prep_lds_bytes(int E, int waves);

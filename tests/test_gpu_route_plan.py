@@ -27,6 +27,21 @@ def test_route_configs(gpu_lib, name):
     _route_case(gpu_lib, ids, cfg["E"])
 
 
+# Batches below 1024 slots run with one ranking wave per 64 slots and a
+# workgroup of those waves plus one per 64 experts: slot counts on both sides
+# of each 64 boundary and of 1024, expert counts on both sides of 64 and
+# beyond 16 * 64, and a few invalid ids among them.
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 127, 512, 1000, 1023, 1024, 1025])
+@pytest.mark.parametrize("E", [1, 12, 64, 65, 1100, 6144])
+def test_route_small_batches(gpu_lib, n, E):
+    g = torch.Generator().manual_seed(n * 7919 + E)
+    ids = torch.randint(0, E, (n, 1), generator=g, dtype=torch.int32)
+    if n > 8:
+        ids[3, 0] = -1
+        ids[n // 2, 0] = E
+    _route_case(gpu_lib, ids, E)
+
+
 @pytest.mark.parametrize("case", ["one_expert", "e1", "sparse", "invalid", "empty", "e1024", "odd"])
 def test_route_adversarial(gpu_lib, case):
     g = torch.Generator().manual_seed(hash(case) % 1000)
