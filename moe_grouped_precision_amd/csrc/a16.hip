@@ -11,7 +11,8 @@
 //
 // The FP4 weights are turned into bf16 in registers (exact: a 2-bit E2M1
 // significand times a power of two or a 4-bit E4M3 significand has at most 6
-// significant bits) and multiplied on the matrix core in bf16
+// significant bits; with E8M0 scales by gfx950's scaled FP4 conversion, two
+// weights per instruction) and multiplied on the matrix core in bf16
 // (v_mfma_f32_16x16x16_bf16, fp32 accumulation).  The weight scale cannot
 // ride in the instruction as the W4A8 path's E8M0 code does, so every weight
 // element pays it in the conversion: this is the scale application the pages
@@ -74,6 +75,18 @@ __device__ __forceinline__ void e2m1x8_to_bf16(uint32_t x, float s, uint32_t (&o
     // the top halves: bf16 of lo in bits 15:0, of hi in bits 31:16
     out[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
   }
+}
+
+// The same for a power-of-two scale s (MXFP4's 2^(code - 127), the subnormal
+// 2^-127 and NaN included): gfx950's scaled conversion turns the two codes
+// of one byte into bf16 times s in one instruction, low nibble into the low
+// half.  It takes only the exponent of s, so E4M3 scales (NVFP4) go through
+// e2m1x8_to_bf16.  Every product is exact in bf16 (2 significant bits).
+__device__ __forceinline__ void e2m1x8_to_bf16_pow2(uint32_t x, float s, uint32_t (&out)[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 0));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 1));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 2));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 3));
 }
 
 // E4M3FN code -> fp32 (exact; 0x7F / 0xFF NaN).
@@ -166,7 +179,10 @@ __device__ __forceinline__ void a16_pass(const uint16_t* __restrict__ A, const u
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         uint32_t t[4];
-        e2m1x8_to_bf16(w0[cb][d], d < 2 ? sa : sb, t);
+        if (FMT == 0)
+          e2m1x8_to_bf16_pow2(w0[cb][d], sa, t);
+        else
+          e2m1x8_to_bf16(w0[cb][d], d < 2 ? sa : sb, t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) wb[cb][4 * d + i] = t[i];
       }
