@@ -13,9 +13,9 @@
 // _dword), which hold no registers while in flight.  Every wave issues the
 // same number of ring loads per stage (blocks past the item's end load with
 // exec = 0), waits for the stage it needs with one explicit vmcnt and meets
-// the others at one barrier per stage.  The depth D grows as the item
-// narrows, so a workgroup keeps about the same weight bytes in flight
-// (8 waves x D stages x NBW blocks x 2 KB: 64-144 KB) whatever its width.
+// the others at one barrier per stage.  The depth D is two stages (four for
+// whole-K items of at most two blocks per wave), so a workgroup keeps 8 waves
+// x D stages x NBW blocks x 2 KB = 64-128 KB of weights in flight.
 // The XOR swizzle that keeps fragment reads free of LDS bank conflicts is
 // applied on the global-address side (a load lane always writes slot base +
 // size * lane).  All loads use clamped addresses (padding rows and columns
@@ -34,9 +34,12 @@ constexpr int P1_KG = 2;
 // (8 * D * NBW) and the paired operands (8 * NBW) share the register file
 constexpr int P1_MAXNBW = 4;
 __host__ __device__ constexpr int stream_max_nbw(int mb) { return mb <= 3 ? 4 : 3; }
-// stages in flight: about 8 block-stages of weights per wave with the whole
-// K per wave; two with the K split (where the LDS holds both parts' rows)
-__host__ __device__ constexpr int stream_depth(int nbw, int ks) { return ks == 2 ? 2 : (nbw <= 2 ? 4 : (nbw == 3 ? 3 : 2)); }
+// stages in flight: two for the shapes items take (three or four blocks per
+// wave with the whole K, any width with the K split): a workgroup then keeps
+// 96-128 KB of weights in flight, and deeper rings only queue more requests
+// at HBM (three stages of three blocks measured slower than two, one stage
+// far slower); four for narrower whole-K items
+__host__ __device__ constexpr int stream_depth(int nbw, int ks) { return ks == 2 || nbw >= 3 ? 2 : 4; }
 // scale chunks (SC groups each) in LDS at once: a chunk is loaded D stages
 // ahead of its first use, while up to D * P1_KG / SC earlier chunks are live
 __host__ __device__ constexpr int stream_nbuf(int nbw, int ks) {

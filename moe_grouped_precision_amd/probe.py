@@ -119,7 +119,10 @@ def mfma_promote_tflops(promote: bool, iters: int = 4096, reps: int = 5, seed: i
 
 def read_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
     """Sustained GB/s of a plain streaming read of nbytes (larger than the
-    last-level cache, so the reads come from HBM)."""
+    last-level cache, so the reads come from HBM): one workgroup of 256
+    threads per CU, eight nontemporal 16-byte loads in flight per thread (32
+    KB per CU), the fastest of the launch shapes measured (more bytes in
+    flight per CU read slower)."""
     lib = load()
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -128,7 +131,7 @@ def read_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def run():
-        st = lib.w4a8_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, cus * 2,
+        st = lib.w4a8_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, cus,
                                  ctypes.c_void_p(sink.data_ptr()), stream)
         if st != 0:
             raise RuntimeError(f"w4a8_probe_read status {st}")
