@@ -17,8 +17,9 @@ namespace w4a8 {
 // small-M schedule below a cutoff (commit 2 "Small-expert seed tile").
 // Constants are this library's own: GRAN is one MFMA block of rows, S_MAX the
 // largest expert the weight-streaming phase serves (four MFMA blocks), T_MAX
-// the MFMA phase's m-tile; TN_STREAM is the n granularity of streaming work
-// (a workgroup item holds 1-3 of these), TN_MFMA the MFMA phase's n-tile.
+// the MFMA phase's m-tile; TN_STREAM is the n granularity by which the plan
+// counts streaming work (a workgroup item spans 1-8 of these), TN_MFMA the
+// MFMA phase's n-tile.
 // ---------------------------------------------------------------------------
 constexpr int GRAN = 16;
 constexpr int S_MAX = 64;
