@@ -96,6 +96,19 @@ def test_a16_without_expert_scales_equals_ones(gpu_lib):
     assert np.array_equal(bits_of(C0), bits_of(C1))
 
 
+def test_a16_mx_scales_across_the_exponent_range(gpu_lib):
+    """MXFP4 scale codes from 2^-107 to 2^93, mixed within every column (one
+    code per 32-K block): the weight operands stay normal bf16 and every sum
+    stays finite in fp32, the range the header states exact, which the
+    kernel's scaled FP4 conversion covers by taking the scale's exponent."""
+    counts, N, K = [17, 40, 5], 96, 512
+    A, B, SB, _, off = _codes_problem(counts, N, K, FMT_MX, seed=77)
+    g = torch.Generator().manual_seed(78)
+    levels = torch.tensor([20, 60, 100, 127, 150, 200, 220], dtype=torch.int32)
+    SB = levels[torch.randint(0, len(levels), tuple(SB.shape), generator=g)].to(torch.uint8)
+    _check(gpu_lib, A, B, SB, FMT_MX, None, off, "MXFP4 scale codes 20..220")
+
+
 @pytest.mark.parametrize("fmt,nan_code", [(FMT_MX, 0xFF), (FMT_NV, 0x7F), (FMT_NV, 0xFF)])
 def test_a16_nan_scales_poison_their_columns(gpu_lib, fmt, nan_code):
     counts, N, K = [6, 21, 3], 64, 256
