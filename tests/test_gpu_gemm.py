@@ -210,6 +210,13 @@ DECODE_ROWS = [0, 0, 1, 3, 5, 5, 6, 6, 7, 7, 7, 8, 9, 9, 11, 14, 15, 15, 16, 17,
     # LDS-table split: 63 and 64 experts of mixed sizes, empty ones included
     ([17, 40, 3, 0, 64, 9, 80] * 9, 1024, 384),
     ([17, 40, 3, 0, 64, 9, 80] * 9 + [33], 1024, 384),
+    # whole-K items of three blocks per wave (17-24 blocks per workgroup) on
+    # the two-stage ring: with one and two row blocks (12 experts), three and
+    # four (18 experts, where one- and two-row-block experts get 29-35 blocks,
+    # some as two items), with one and three K groups (one- and two-stage
+    # loops; fewer groups than a scale chunk)
+    ([5, 9, 17, 30, 44, 64, 1, 12, 23, 50, 60, 33], 6144, 128),
+    ([40, 47, 5, 9, 17, 30, 44, 64, 1, 12, 23, 50, 60, 33, 36, 41, 20, 8], 6144, 384),
 ])
 def test_ragged_and_edge_shapes(gpu_lib, counts, N, K):
     _codes_case(gpu_lib, counts, N, K, seed=sum(counts) + N)
